@@ -1,0 +1,62 @@
+"""Seeded input generator: determinism, shapes, dtypes and distributions (CPU)."""
+import math
+
+import numpy as np
+import torch
+
+from mamba_ssd_scan_04_amd import inputs
+
+
+def test_workloads_match_layer_shapes():
+    w = inputs.WORKLOADS
+    assert (w["m2p7"].batch, w["m2p7"].seqlen, w["m2p7"].nheads, w["m2p7"].headdim,
+            w["m2p7"].dstate, w["m2p7"].chunk_size) == (8, 4096, 80, 64, 128, 256)
+    assert w["m2p7"].nheads * w["m2p7"].headdim == 5120
+    assert w["m125"].nheads * w["m125"].headdim == 1536
+    assert w["long16k"].seqlen == 16384 and w["long16k"].dt_shift == 4.0
+    for n in (16, 64, 128, 256):
+        s = w[f"nsweep{n}"]
+        assert s.dstate == n and s.ngroups == 8 and s.nheads // s.ngroups == 3
+    assert w["tiny"].dtype == "fp32"
+
+
+def test_deterministic_and_typed():
+    w = inputs.WORKLOADS["tiny"]
+    a, b = inputs.generate(w, seed=0), inputs.generate(w, seed=0)
+    c = inputs.generate(w, seed=1)
+    for k in a:
+        assert torch.equal(a[k], b[k])
+    assert not torch.equal(a["x"], c["x"])
+    assert a["x"].shape == (1, 256, 2, 16) and a["x"].dtype == torch.float32
+    assert a["B"].shape == (1, 256, 1, 16)
+    w2 = inputs.WORKLOADS["m125"].replace(batch=1, seqlen=512)
+    d = inputs.generate(w2)
+    assert d["x"].dtype == torch.bfloat16 and d["dt"].dtype == torch.float32
+    assert d["A"].shape == (24,) and d["D"].shape == (24,)
+
+
+def test_distributions():
+    w = inputs.WORKLOADS["m125"].replace(batch=2, seqlen=1024)
+    d = inputs.generate(w)
+    dt = d["dt"].numpy()
+    assert dt.min() > 0
+    # E[softplus(z - 2)] for z ~ N(0, 1) is about 0.18
+    assert 0.16 < dt.mean() < 0.20
+    A = d["A"].numpy()
+    assert np.all(A <= -1.0 + 1e-6) and np.all(A >= -16.0 - 1e-4)
+    Bs = d["B"].float().numpy()
+    assert abs(Bs.std() * math.sqrt(w.dstate) - 1.0) < 0.02
+    x = d["x"].float().numpy()
+    assert abs(x.mean()) < 0.01 and abs(x.std() - 1.0) < 0.01
+    slow = inputs.generate_slow_decay(w)
+    assert np.all(slow["A"].numpy() > -0.1) and np.all(slow["A"].numpy() < -1e-3)
+    assert torch.equal(slow["x"], d["x"])
+
+
+def test_float64_upcast_is_exact():
+    w = inputs.WORKLOADS["m125"].replace(batch=1, seqlen=64)
+    d = inputs.generate(w)
+    f = inputs.to_float64(d)
+    assert f["x"].dtype == np.float64
+    back = torch.from_numpy(f["x"]).to(torch.bfloat16)
+    assert torch.equal(back, d["x"])
