@@ -1,0 +1,243 @@
+"""Benchmark: SSD chunked forward tokens/s on one MI355X, with roofline.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload m2p7]
+                    [--state-dtype fp32|bf16] [--no-cpu-baseline]
+
+One step is one pass of the whole path (ssd_chunk_cumsum, ssd_chunk_state,
+ssd_state_passing, ssd_chunk_scan: the four launches ssd_forward makes) over
+one batch of seeded synthetic input already resident in HBM. The timed region
+issues the four stage entry points with HIP events between them on the launch
+stream, so every kernel's average duration is measured inside the same region
+whose wall clock gives tokens/s. Rank 0 prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "SSD fwd tokens/sec at 2.7B-layer shape (L=4096, N=128); % MFMA/HBM roofline"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFS = 2500.0  # dense bf16, TFLOP/s
+MFMA_F32_PEAK_TFS = 157.3
+KERNELS = ["ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan"]
+SOURCES = {"ssd_chunk_cumsum": "chunk_cumsum.hip", "ssd_chunk_state": "chunk_state.hip",
+           "ssd_state_passing": "state_passing.hip", "ssd_chunk_scan": "chunk_scan.hip"}
+
+
+def kernel_work(w, state_bytes: int) -> dict:
+    """Algorithmic bytes and flops per launch of each kernel (the bytes each
+    must move at minimum given its inputs and outputs, and the flops of the
+    method's contractions: causal lower triangle incl. the diagonal, C B^T
+    once per group)."""
+    b, T, H, P, N, G, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk_size
+    nc = w.nchunks
+    e = 2 if w.dtype == "bf16" else 4
+    st = b * nc * H * N * P * state_bytes           # one pass over the chunk states
+    st_in = b * (nc - 1) * H * N * P * state_bytes  # carried states read (h_0 = 0 is known)
+    Qc = T / nc                                      # mean chunk length
+    return {
+        "ssd_chunk_cumsum": {"bytes": 4 * b * T * H + 4 * b * H * nc * Q, "flops": b * T * H},
+        "ssd_chunk_state": {"bytes": e * b * T * (H * P + G * N) + 8 * b * T * H + st,
+                            "flops": 2 * b * T * H * N * P},
+        "ssd_state_passing": {"bytes": 2 * st + 4 * b * H * N * P + 4 * b * H * nc,
+                              "flops": 2 * b * nc * H * N * P},
+        "ssd_chunk_scan": {"bytes": e * b * T * (2 * H * P + 2 * G * N) + 8 * b * T * H + st_in,
+                           "flops": int(b * nc * (G * N * Qc * (Qc + 1) + H * P * Qc * (Qc + 1))
+                                        + 2 * b * (T - Q) * H * N * P)},
+    }
+
+
+def source_sha(kernel: str) -> str:
+    path = os.path.join(ROOT, "mamba_ssd_scan_04_amd", "csrc", SOURCES[kernel])
+    h = hashlib.sha256()
+    for p in (path, os.path.join(ROOT, "mamba_ssd_scan_04_amd", "csrc", "ssd_common.hpp"),
+              os.path.join(ROOT, "mamba_ssd_scan_04_amd", "csrc", "transpose.hpp")):
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str, state_dtype: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"pmc_{kernel}_{workload}_{state_dtype}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha") != source_sha(kernel):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, w, budget_s: float = 10.0) -> dict:
+    """Time the fp64 oracle on a bounded sample of the same workload: whole
+    (batch, head) sequences, as many as fit about `budget_s` seconds."""
+    import oracle
+    from mamba_ssd_scan_04_amd import inputs as gen
+
+    threads = max(1, min(16, oracle.default_threads()))
+    hpg = w.nheads // w.ngroups
+
+    def run(npairs):
+        pairs = [(i // w.nheads, i % w.nheads) for i in range(npairs)]
+        # one batch element's heads at a time; the oracle threads over heads
+        tot = 0.0
+        done = 0
+        for bi in sorted({p[0] for p in pairs}):
+            hs = [h for (bb, h) in pairs if bb == bi]
+            h0, h1 = hs[0], hs[-1] + 1
+            g0, g1 = h0 // hpg, (h1 - 1) // hpg + 1
+            sl = {"x": inp["x"][bi:bi + 1, :, h0:h1], "dt": inp["dt"][bi:bi + 1, :, h0:h1],
+                  "A": inp["A"][h0:h1], "B": inp["B"][bi:bi + 1, :, g0:g1],
+                  "C": inp["C"][bi:bi + 1, :, g0:g1], "D": inp["D"][h0:h1]}
+            f = gen.to_float64(sl)
+            if g1 - g0 > 1 or w.ngroups > 1:
+                # map the sliced heads onto their groups explicitly
+                idx = [h // hpg - g0 for h in range(h0, h1)]
+                f["B"], f["C"] = f["B"][:, :, idx], f["C"][:, :, idx]
+            t0 = time.perf_counter()
+            oracle.recurrence(f["x"], f["dt"], f["A"], f["B"], f["C"], f["D"], nthreads=threads)
+            tot += time.perf_counter() - t0
+            done += h1 - h0
+        return tot, done
+
+    probe_pairs = min(threads, w.batch * w.nheads)
+    t_probe, _ = run(probe_pairs)
+    per_pair = t_probe / probe_pairs * threads  # thread-seconds per pair
+    target = int(budget_s * threads / max(per_pair, 1e-9))
+    npairs = max(probe_pairs, min(w.batch * w.nheads, target))
+    npairs = (npairs // threads) * threads or npairs
+    secs, done = run(npairs)
+    tokens_equiv = done * w.seqlen / w.nheads
+    return {"value": tokens_equiv / secs, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} whole (batch, head) sequences of {w.seqlen} tokens "
+                      f"({done / w.nheads:.2f} batch elements' worth of the {w.nheads}-head layer), "
+                      f"fp64 recurrence in {secs:.2f} s on {threads} threads; tokens/s = sequences*T/H/s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="m2p7")
+    ap.add_argument("--state-dtype", default="fp32", choices=["fp32", "bf16"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(no collectives); run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import mamba_ssd_scan_04_amd as ssd
+    from mamba_ssd_scan_04_amd import inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    w = inputs.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    inp = inputs.generate(w, seed=0)
+    g = {k: v.to(dev) for k, v in inp.items()}
+    d = ssd.dims_of(g["x"], g["B"], w.chunk_size, args.state_dtype)
+    sbytes = 2 if args.state_dtype == "bf16" else 4
+    cs = torch.empty((w.batch, w.nheads, w.nchunks, w.chunk_size), dtype=torch.float32, device=dev)
+    states = torch.empty((w.batch, w.nchunks, w.nheads, w.headdim, w.dstate),
+                         dtype=torch.bfloat16 if sbytes == 2 else torch.float32, device=dev)
+    final = torch.empty((w.batch, w.nheads, w.dstate, w.headdim), dtype=torch.float32, device=dev)
+    y = torch.empty_like(g["x"])
+    ws = ssd.alloc_workspace(d, dev)
+    stream = torch.cuda.current_stream(dev)
+    sh = stream.cuda_stream
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        ssd.ssd_chunk_cumsum(d, g["dt"], g["A"], cs, sh)
+        if ev is not None:
+            ev[1].record(stream)
+        ssd.ssd_chunk_state(d, g["x"], g["dt"], g["B"], cs, states, sh)
+        if ev is not None:
+            ev[2].record(stream)
+        ssd.ssd_state_passing(d, cs, states, final, sh)
+        if ev is not None:
+            ev[3].record(stream)
+        ssd.ssd_chunk_scan(d, g["x"], g["dt"], g["B"], g["C"], g["D"], cs, states, y, sh)
+        if ev is not None:
+            ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+    kms = {name: sum(events[k][i].elapsed_time(events[k][i + 1]) for k in range(args.steps)) / args.steps
+           for i, name in enumerate(KERNELS)}
+
+    # the same four launches through ssd_forward, for reference
+    for _ in range(args.warmup):
+        ssd.ssd_forward(d, g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], y, final, ws, ws.numel(), sh)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(args.steps):
+        ssd.ssd_forward(d, g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], y, final, ws, ws.numel(), sh)
+    torch.cuda.synchronize()
+    fwd_ms = (time.perf_counter() - t1) * 1e3 / args.steps
+
+    work = kernel_work(w, sbytes)
+    peak_tf = MFMA_BF16_PEAK_TFS if w.dtype == "bf16" else MFMA_F32_PEAK_TFS
+    per_kernel = {}
+    for name in KERNELS:
+        t = kms[name] * 1e-3
+        gbs = work[name]["bytes"] / t / 1e9
+        tfs = work[name]["flops"] / t / 1e12
+        per_kernel[name] = {"ms": round(kms[name], 5), "GB/s": round(gbs, 1),
+                            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                            "TFLOP/s": round(tfs, 2), "mfma_frac": round(tfs / peak_tf, 4),
+                            "alg_bytes": work[name]["bytes"], "alg_flops": work[name]["flops"]}
+    dom = max(KERNELS, key=lambda n: kms[n])
+    traffic = measured_traffic(dom, w.name, args.state_dtype)
+    roof = {"kernel": dom, "bound": "hbm", "achieved": per_kernel[dom]["GB/s"], "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": per_kernel[dom]["hbm_frac"], "traffic": traffic}
+    tokens = w.batch * w.seqlen
+    value = tokens / (ms_per_step * 1e-3)
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: Mamba-2 2.7B-layer SSD shape" if w.name == "m2p7" else w.name,
+                   "batch": w.batch, "seqlen": w.seqlen, "nheads": w.nheads, "headdim": w.headdim,
+                   "dstate": w.dstate, "ngroups": w.ngroups, "chunk_size": w.chunk_size,
+                   "state_dtype": args.state_dtype, "tokens_per_step": tokens},
+        "roofline": roof,
+        "kernels": per_kernel,
+        "forward_ms_per_step": round(fwd_ms, 5),
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, w, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,158 @@
+/*
+ * libssd: the SSD (state space duality) chunked sequence transform on MI355X.
+ *
+ * The operation ("Transformers are SSMs", Dao & Gu; Knowl 1 of the chapterpal
+ * summary) maps, per batch element and head h (group g = h / (H / G)):
+ *
+ *   h_t = exp(dt_t * A_h) * h_{t-1} + dt_t * B_t x_t^T,  h_{-1} = 0   (N x P)
+ *   y_t = C_t^T h_t + D_h * x_t
+ *
+ * and is evaluated by the block decomposition of Knowl 2: chunks of Q tokens,
+ * the masked quadratic form (L o C B^T) X inside each chunk, a scalar linear
+ * recurrence on N x P chunk states between chunks. Heads of one group share
+ * B and C (Knowl 7, the multi-input / grouped-input patterns).
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers to contiguous row-major arrays,
+ *    16-byte aligned. The caller owns every buffer; the library never
+ *    allocates, frees or keeps a pointer, holds no state between calls, and is
+ *    safe to call from several threads.
+ *  - Arguments are checked synchronously. On any error the call returns a
+ *    status and launches nothing. On success the kernels are enqueued on
+ *    `stream` (0 = the null stream) and the call returns without waiting;
+ *    device faults surface at the caller's stream synchronisation.
+ *  - Data values are never inspected: NaN and Inf propagate. A_h > 0 is
+ *    computed as written (the pages take a_t in [0, 1]).
+ *  - Sizes: batch >= 0, seqlen >= 0 (0 gives a zero final state), nheads,
+ *    ngroups >= 1 with nheads % ngroups == 0; headdim P in {16, 32, 64, 128};
+ *    dstate N in {16, 32, 64, 128, 256}; chunk_size Q in {32, 64, 128, 256}.
+ *    seqlen need not be a multiple of Q: the last chunk may be shorter.
+ *
+ * Tensor layouts (b = batch, T = seqlen, H = nheads, P = headdim, N = dstate,
+ * G = ngroups, nc = ceil(T / Q)):
+ *    x, y        [b, T, H, P]   dtype (fp32 or bf16)
+ *    dt          [b, T, H]      fp32, the step size (softplus already applied)
+ *    A, D        [H]            fp32
+ *    B, C        [b, T, G, N]   dtype
+ *    final_state [b, H, N, P]   fp32
+ *    cs          [b, H, nc, Q]  fp32  (stage buffer, see ssd_chunk_cumsum)
+ *    states      [b, nc, H, P, N] state dtype (stage buffer; note P before N)
+ */
+#ifndef LIBSSD_SSD_H
+#define LIBSSD_SSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSD_ABI_VERSION 1
+
+typedef enum {
+    SSD_OK = 0,
+    SSD_ERR_NULL_POINTER = 1,        /* a required pointer is NULL */
+    SSD_ERR_BAD_SHAPE = 2,           /* negative or zero size, or nheads % ngroups != 0 */
+    SSD_ERR_UNSUPPORTED = 3,         /* headdim/dstate/chunk_size/dtype outside the lists above */
+    SSD_ERR_MISALIGNED = 4,          /* a tensor pointer is not 16-byte aligned */
+    SSD_ERR_WORKSPACE_TOO_SMALL = 5, /* workspace_bytes < ssd_workspace_size() */
+    SSD_ERR_LAUNCH = 6               /* the HIP runtime rejected a launch */
+} ssd_status;
+
+typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
+
+typedef struct {
+    int64_t batch;       /* b */
+    int64_t seqlen;      /* T */
+    int64_t nheads;      /* H */
+    int64_t headdim;     /* P */
+    int64_t dstate;      /* N */
+    int64_t ngroups;     /* G: heads [g*H/G, (g+1)*H/G) share B[..., g, :] and C[..., g, :] */
+    int64_t chunk_size;  /* Q */
+    int32_t dtype;       /* ssd_dtype of x, B, C and y */
+    int32_t state_dtype; /* ssd_dtype of the inter-chunk states in the workspace; SSD_BF16
+                            only with dtype == SSD_BF16. The final state is always fp32. */
+} ssd_dims;
+
+/* Version of this interface (SSD_ABI_VERSION). */
+int ssd_abi_version(void);
+
+/* Text for a status code (static storage; never NULL). */
+const char* ssd_status_string(ssd_status s);
+
+/* Checks `d` alone (no pointers): SSD_OK or the error ssd_forward would give. */
+ssd_status ssd_check_dims(const ssd_dims* d);
+
+/* Bytes of device workspace ssd_forward needs for `d`; 0 when `d` is invalid
+ * (and for batch == 0 or seqlen == 0, which need none). The workspace holds
+ * the cs buffer and the states buffer below, each at a 256-byte aligned offset. */
+size_t ssd_workspace_size(const ssd_dims* d);
+
+/* Bytes of the two stage buffers for the stage entry points: cs [b,H,nc,Q] fp32
+ * and states [b,nc,H,P,N] in d->state_dtype. Either output pointer may be NULL.
+ * Returns ssd_check_dims(d). */
+ssd_status ssd_stage_sizes(const ssd_dims* d, size_t* cs_bytes, size_t* states_bytes);
+
+/*
+ * Full forward: Knowl 2's inputs X, A, B, C and chunk size Q, its outputs Y and
+ * h_final ("Input"/"Output" lines of the algorithm), with the per-head
+ * discretisation dt, A and the skip term D. Enqueues, in order,
+ * ssd_chunk_cumsum, ssd_chunk_state, ssd_state_passing and ssd_chunk_scan.
+ *   x [b,T,H,P], dt [b,T,H], A [H], B [b,T,G,N], C [b,T,G,N], D [H]: inputs
+ *   y [b,T,H,P] (out, dtype), final_state [b,H,N,P] (out, fp32)
+ *   workspace: device buffer of at least ssd_workspace_size(d) bytes; its
+ *   contents on entry do not matter and are garbage on return.
+ * y must not overlap any input. */
+ssd_status ssd_forward(const ssd_dims* d, const void* x, const float* dt, const float* A,
+                       const void* B, const void* C, const float* D, void* y,
+                       float* final_state, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
+
+/*
+ * Stage 1 (Knowl 2, "intra-chunk cumulative products of A", taken in log
+ * space): cs[b,h,c,j] = sum_{s=0..j} dt[b,cQ+s,h] * A[h], an inclusive prefix
+ * sum per chunk, so exp(cs) is the cumulative product of a. Positions past the
+ * end of a short last chunk repeat its last value (padding tokens have dt = 0).
+ *   dt [b,T,H], A [H] in; cs [b,H,nc,Q] fp32 out.
+ */
+ssd_status ssd_chunk_cumsum(const ssd_dims* d, const float* dt, const float* A, float* cs,
+                            hipStream_t stream);
+
+/*
+ * Stage 2 (Knowl 2, "right factor chunk state" S = B^T (decayed X)):
+ *   states[b,c,h,p,n] = sum_j B[b,cQ+j,g,n] * exp(cs_last - cs_j) * dt[b,cQ+j,h] * x[b,cQ+j,h,p]
+ * where cs_last is the chunk's last cs value: each token is decayed to the end
+ * of its chunk. bf16 MFMA (fp32 MFMA for fp32 inputs), fp32 accumulation.
+ *   x, dt, B, cs in; states [b,nc,H,P,N] out (transposed N x P matrices).
+ */
+ssd_status ssd_chunk_state(const ssd_dims* d, const void* x, const float* dt, const void* B,
+                           const float* cs, void* states, hipStream_t stream);
+
+/*
+ * Stage 3 (Knowl 2, the sequential loop over chunks h_{c+1} = (prod a) h_c + S_c,
+ * h_0 = 0, h_final = h_{T/Q}): in place, states[c] (S_c on entry) is replaced by
+ * the state entering chunk c (h_c; zero for c = 0), and final_state [b,H,N,P]
+ * receives h_{nc} in fp32. The running state is kept in fp32.
+ */
+ssd_status ssd_state_passing(const ssd_dims* d, const float* cs, void* states,
+                             float* final_state, hipStream_t stream);
+
+/*
+ * Stage 4 (Knowl 2, diagonal-block outputs (L o C B^T) X, the off-diagonal
+ * output C (decayed h_c) and their sum; plus D * x):
+ *   y[t=cQ+j] = sum_{i<=j} (C_j . B_i) exp(cs_j - cs_i) dt_i x_i
+ *             + exp(cs_j) C_j^T h_c + D_h x_j
+ * with states holding h_c as written by ssd_state_passing.
+ */
+ssd_status ssd_chunk_scan(const ssd_dims* d, const void* x, const float* dt, const void* B,
+                          const void* C, const float* D, const float* cs, const void* states,
+                          void* y, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBSSD_SSD_H */

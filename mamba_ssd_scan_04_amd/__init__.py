@@ -1,0 +1,212 @@
+"""Python binding of libssd, the MI355X (gfx950) SSD chunked forward.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/ssd.h. PyTorch supplies device
+memory and the current stream. The functions named like the C entry points
+(`ssd_forward`, `ssd_chunk_cumsum`, ...) take caller-allocated tensors; the
+helpers `forward` and `stages` allocate outputs with torch first.
+
+Raises RuntimeError if libssd.so has not been built (python -m
+mamba_ssd_scan_04_amd.build): there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libssd.so")
+
+SSD_F32, SSD_BF16 = 0, 1
+_DTYPE_CODE = {torch.float32: SSD_F32, torch.bfloat16: SSD_BF16}
+_STATE_CODE = {"fp32": SSD_F32, "bf16": SSD_BF16}
+
+
+class SsdDims(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int64),
+        ("seqlen", ctypes.c_int64),
+        ("nheads", ctypes.c_int64),
+        ("headdim", ctypes.c_int64),
+        ("dstate", ctypes.c_int64),
+        ("ngroups", ctypes.c_int64),
+        ("chunk_size", ctypes.c_int64),
+        ("dtype", ctypes.c_int32),
+        ("state_dtype", ctypes.c_int32),
+    ]
+
+    @property
+    def nchunks(self) -> int:
+        return -(-self.seqlen // self.chunk_size)
+
+
+_lib = None
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libssd.so (once). Fails loudly when it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"libssd.so not found at {LIB_PATH}; build it with "
+                           "`python -m mamba_ssd_scan_04_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER(SsdDims)
+    vp, sz, st = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    lib.ssd_abi_version.argtypes, lib.ssd_abi_version.restype = [], ctypes.c_int
+    lib.ssd_status_string.argtypes, lib.ssd_status_string.restype = [st], ctypes.c_char_p
+    lib.ssd_check_dims.argtypes, lib.ssd_check_dims.restype = [P], st
+    lib.ssd_workspace_size.argtypes, lib.ssd_workspace_size.restype = [P], sz
+    lib.ssd_stage_sizes.argtypes = [P, ctypes.POINTER(sz), ctypes.POINTER(sz)]
+    lib.ssd_stage_sizes.restype = st
+    lib.ssd_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.ssd_forward.restype = st
+    lib.ssd_chunk_cumsum.argtypes, lib.ssd_chunk_cumsum.restype = [P, vp, vp, vp, vp], st
+    lib.ssd_chunk_state.argtypes, lib.ssd_chunk_state.restype = [P, vp, vp, vp, vp, vp, vp], st
+    lib.ssd_state_passing.argtypes, lib.ssd_state_passing.restype = [P, vp, vp, vp, vp], st
+    lib.ssd_chunk_scan.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.ssd_chunk_scan.restype = st
+    _lib = lib
+    return lib
+
+
+class SsdError(RuntimeError):
+    def __init__(self, code: int):
+        self.code = code
+        msg = load_library().ssd_status_string(code).decode()
+        super().__init__(f"libssd status {code}: {msg}")
+
+
+def _check(code: int) -> None:
+    if code != 0:
+        raise SsdError(code)
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_contiguous():
+        raise ValueError("libssd needs contiguous tensors")
+    return t.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def make_dims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype="bf16",
+              state_dtype="fp32") -> SsdDims:
+    dt_code = dtype if isinstance(dtype, int) else (
+        _DTYPE_CODE[dtype] if isinstance(dtype, torch.dtype) else _STATE_CODE[dtype])
+    return SsdDims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dt_code,
+                   _STATE_CODE[state_dtype] if isinstance(state_dtype, str) else state_dtype)
+
+
+def dims_of(x: torch.Tensor, B: torch.Tensor, chunk_size: int, state_dtype="fp32") -> SsdDims:
+    b, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    if x.dtype not in _DTYPE_CODE:
+        raise TypeError(f"x must be float32 or bfloat16, got {x.dtype}")
+    return make_dims(b, T, H, P, N, G, chunk_size, x.dtype, state_dtype)
+
+
+# ---- the C entry points, one to one ------------------------------------------
+
+def ssd_abi_version() -> int:
+    return load_library().ssd_abi_version()
+
+
+def ssd_status_string(code: int) -> str:
+    return load_library().ssd_status_string(code).decode()
+
+
+def ssd_check_dims(d: SsdDims) -> int:
+    return load_library().ssd_check_dims(ctypes.byref(d))
+
+
+def ssd_workspace_size(d: SsdDims) -> int:
+    return load_library().ssd_workspace_size(ctypes.byref(d))
+
+
+def ssd_stage_sizes(d: SsdDims) -> tuple[int, int]:
+    cs, st = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check(load_library().ssd_stage_sizes(ctypes.byref(d), ctypes.byref(cs), ctypes.byref(st)))
+    return cs.value, st.value
+
+
+def ssd_forward(d, x, dt, A, B, C, D, y, final_state, workspace, workspace_bytes, stream=None):
+    s = _stream(x.device) if stream is None else stream
+    _check(load_library().ssd_forward(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
+                                      _ptr(C), _ptr(D), _ptr(y), _ptr(final_state),
+                                      _ptr(workspace), workspace_bytes, s))
+
+
+def ssd_chunk_cumsum(d, dt, A, cs, stream=None):
+    s = _stream(dt.device) if stream is None else stream
+    _check(load_library().ssd_chunk_cumsum(ctypes.byref(d), _ptr(dt), _ptr(A), _ptr(cs), s))
+
+
+def ssd_chunk_state(d, x, dt, B, cs, states, stream=None):
+    s = _stream(x.device) if stream is None else stream
+    _check(load_library().ssd_chunk_state(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(B), _ptr(cs),
+                                          _ptr(states), s))
+
+
+def ssd_state_passing(d, cs, states, final_state, stream=None):
+    s = _stream(final_state.device) if stream is None else stream
+    _check(load_library().ssd_state_passing(ctypes.byref(d), _ptr(cs), _ptr(states),
+                                            _ptr(final_state), s))
+
+
+def ssd_chunk_scan(d, x, dt, B, C, D, cs, states, y, stream=None):
+    s = _stream(x.device) if stream is None else stream
+    _check(load_library().ssd_chunk_scan(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(B), _ptr(C),
+                                         _ptr(D), _ptr(cs), _ptr(states), _ptr(y), s))
+
+
+# ---- allocating helpers -------------------------------------------------------
+
+def _state_torch_dtype(d: SsdDims) -> torch.dtype:
+    return torch.bfloat16 if d.state_dtype == SSD_BF16 else torch.float32
+
+
+def alloc_workspace(d: SsdDims, device) -> torch.Tensor:
+    n = ssd_workspace_size(d)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+
+
+def forward(x, dt, A, B, C, D, chunk_size: int, state_dtype: str = "fp32", workspace=None):
+    """y, final_state = SSD(x, dt, A, B, C, D) through ssd_forward."""
+    d = dims_of(x, B, chunk_size, state_dtype)
+    _check(ssd_check_dims(d))
+    y = torch.empty_like(x)
+    final = torch.empty((d.batch, d.nheads, d.dstate, d.headdim), dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = alloc_workspace(d, x.device)
+    ssd_forward(d, x, dt, A, B, C, D, y, final, workspace, workspace.numel())
+    return y, final
+
+
+def stages(x, dt, A, B, C, D, chunk_size: int, state_dtype: str = "fp32"):
+    """Run the four stage entry points one by one and return every intermediate:
+    cs [b,H,nc,Q], S [b,nc,H,P,N] (chunk states, before passing), h_in (same
+    layout: state entering each chunk), final [b,H,N,P], y."""
+    d = dims_of(x, B, chunk_size, state_dtype)
+    _check(ssd_check_dims(d))
+    dev = x.device
+    b, H, P, N, nc, Q = d.batch, d.nheads, d.headdim, d.dstate, d.nchunks, d.chunk_size
+    cs = torch.empty((b, H, nc, Q), dtype=torch.float32, device=dev)
+    states = torch.empty((b, nc, H, P, N), dtype=_state_torch_dtype(d), device=dev)
+    final = torch.empty((b, H, N, P), dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+    ssd_chunk_cumsum(d, dt, A, cs)
+    ssd_chunk_state(d, x, dt, B, cs, states)
+    S = states.clone()
+    ssd_state_passing(d, cs, states, final)
+    ssd_chunk_scan(d, x, dt, B, C, D, cs, states, y)
+    return {"cs": cs, "S": S, "h_in": states, "final": final, "y": y}

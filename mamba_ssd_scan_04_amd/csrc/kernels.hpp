@@ -1,0 +1,17 @@
+// Host-side launchers of the four SSD kernels (each in its own .hip file).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "ssd_common.hpp"
+
+namespace ssd {
+
+// dtype/state dtype codes follow ssd_dtype: 0 = fp32, 1 = bf16.
+hipError_t launch_chunk_cumsum(const Params& p, hipStream_t s);
+hipError_t launch_chunk_state(const Params& p, int dtype, int state_dtype, hipStream_t s);
+hipError_t launch_state_passing(const Params& p, int state_dtype, hipStream_t s);
+hipError_t launch_chunk_scan(const Params& p, int dtype, int state_dtype, hipStream_t s);
+hipError_t launch_zero_fill(float* dst, int64_t n, hipStream_t s);
+
+}  // namespace ssd

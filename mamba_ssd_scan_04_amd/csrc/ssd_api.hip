@@ -1,0 +1,208 @@
+// The C ABI of libssd (declared in include/ssd.h): argument checks, workspace
+// layout and the launch order of the four kernels. No allocation, no state.
+#include <stdint.h>
+
+#include "../../include/ssd.h"
+#include "kernels.hpp"
+
+namespace ssd {
+int chunk_scan_lds_bytes(int dtype, int64_t P, int64_t N, int64_t Q);
+}
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxLds = 160 * 1024;
+
+size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool in_list(int64_t v, const int64_t* list, int n) {
+    for (int i = 0; i < n; ++i)
+        if (list[i] == v) return true;
+    return false;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t nchunks_of(const ssd_dims* d) { return (d->seqlen + d->chunk_size - 1) / d->chunk_size; }
+
+size_t cs_bytes_of(const ssd_dims* d) {
+    return (size_t)d->batch * d->nheads * nchunks_of(d) * d->chunk_size * sizeof(float);
+}
+
+size_t states_bytes_of(const ssd_dims* d) {
+    const size_t esz = d->state_dtype == SSD_BF16 ? 2 : 4;
+    return (size_t)d->batch * nchunks_of(d) * d->nheads * d->headdim * d->dstate * esz;
+}
+
+ssd::Params make_params(const ssd_dims* d) {
+    ssd::Params p{};
+    p.batch = d->batch;
+    p.seqlen = d->seqlen;
+    p.nheads = d->nheads;
+    p.headdim = d->headdim;
+    p.dstate = d->dstate;
+    p.ngroups = d->ngroups;
+    p.chunk = d->chunk_size;
+    p.nchunks = nchunks_of(d);
+    p.heads_per_group = d->nheads / d->ngroups;
+    return p;
+}
+
+ssd_status to_status(hipError_t e) { return e == hipSuccess ? SSD_OK : SSD_ERR_LAUNCH; }
+
+bool empty(const ssd_dims* d) { return d->batch == 0 || d->seqlen == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int ssd_abi_version(void) { return SSD_ABI_VERSION; }
+
+const char* ssd_status_string(ssd_status s) {
+    switch (s) {
+        case SSD_OK: return "ok";
+        case SSD_ERR_NULL_POINTER: return "a required pointer is NULL";
+        case SSD_ERR_BAD_SHAPE: return "bad shape: negative or zero size, or nheads not divisible by ngroups";
+        case SSD_ERR_UNSUPPORTED:
+            return "unsupported configuration: headdim in {16,32,64,128}, dstate in {16,32,64,128,256}, "
+                   "chunk_size in {32,64,128,256}, dtype fp32/bf16, bf16 states only with bf16 inputs, "
+                   "and (fp32) the chunk tile must fit in LDS";
+        case SSD_ERR_MISALIGNED: return "a tensor pointer is not 16-byte aligned";
+        case SSD_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than ssd_workspace_size()";
+        case SSD_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
+    }
+    return "unknown status";
+}
+
+ssd_status ssd_check_dims(const ssd_dims* d) {
+    static const int64_t kP[] = {16, 32, 64, 128};
+    static const int64_t kN[] = {16, 32, 64, 128, 256};
+    static const int64_t kQ[] = {32, 64, 128, 256};
+    if (!d) return SSD_ERR_NULL_POINTER;
+    if (d->batch < 0 || d->seqlen < 0 || d->nheads <= 0 || d->headdim <= 0 || d->dstate <= 0 ||
+        d->ngroups <= 0 || d->chunk_size <= 0)
+        return SSD_ERR_BAD_SHAPE;
+    if (d->nheads % d->ngroups != 0) return SSD_ERR_BAD_SHAPE;
+    if (!in_list(d->headdim, kP, 4) || !in_list(d->dstate, kN, 5) || !in_list(d->chunk_size, kQ, 4))
+        return SSD_ERR_UNSUPPORTED;
+    if (d->dtype != SSD_F32 && d->dtype != SSD_BF16) return SSD_ERR_UNSUPPORTED;
+    if (d->state_dtype != SSD_F32 && d->state_dtype != SSD_BF16) return SSD_ERR_UNSUPPORTED;
+    if (d->state_dtype == SSD_BF16 && d->dtype != SSD_BF16) return SSD_ERR_UNSUPPORTED;
+    if (ssd::chunk_scan_lds_bytes(d->dtype, d->headdim, d->dstate, d->chunk_size) > kMaxLds)
+        return SSD_ERR_UNSUPPORTED;
+    // grid limits: nchunks and nheads go in grid.x / grid.y, batch in grid.z
+    if (nchunks_of(d) > INT32_MAX || d->nheads > 65535 || d->batch > 65535) return SSD_ERR_UNSUPPORTED;
+    return SSD_OK;
+}
+
+ssd_status ssd_stage_sizes(const ssd_dims* d, size_t* cs_bytes, size_t* states_bytes) {
+    const ssd_status st = ssd_check_dims(d);
+    if (st != SSD_OK) return st;
+    if (cs_bytes) *cs_bytes = cs_bytes_of(d);
+    if (states_bytes) *states_bytes = states_bytes_of(d);
+    return SSD_OK;
+}
+
+size_t ssd_workspace_size(const ssd_dims* d) {
+    if (ssd_check_dims(d) != SSD_OK || empty(d)) return 0;
+    return round_up(cs_bytes_of(d)) + round_up(states_bytes_of(d));
+}
+
+ssd_status ssd_chunk_cumsum(const ssd_dims* d, const float* dt, const float* A, float* cs,
+                            hipStream_t stream) {
+    ssd_status st = ssd_check_dims(d);
+    if (st != SSD_OK) return st;
+    if (empty(d)) return SSD_OK;
+    if (!dt || !A || !cs) return SSD_ERR_NULL_POINTER;
+    if (!aligned16(dt) || !aligned16(A) || !aligned16(cs)) return SSD_ERR_MISALIGNED;
+    ssd::Params p = make_params(d);
+    p.dt = dt;
+    p.A = A;
+    p.cs = cs;
+    return to_status(ssd::launch_chunk_cumsum(p, stream));
+}
+
+ssd_status ssd_chunk_state(const ssd_dims* d, const void* x, const float* dt, const void* B,
+                           const float* cs, void* states, hipStream_t stream) {
+    ssd_status st = ssd_check_dims(d);
+    if (st != SSD_OK) return st;
+    if (empty(d)) return SSD_OK;
+    if (!x || !dt || !B || !cs || !states) return SSD_ERR_NULL_POINTER;
+    if (!aligned16(x) || !aligned16(dt) || !aligned16(B) || !aligned16(cs) || !aligned16(states))
+        return SSD_ERR_MISALIGNED;
+    ssd::Params p = make_params(d);
+    p.x = x;
+    p.dt = dt;
+    p.B = B;
+    p.cs = const_cast<float*>(cs);
+    p.states = states;
+    return to_status(ssd::launch_chunk_state(p, d->dtype, d->state_dtype, stream));
+}
+
+ssd_status ssd_state_passing(const ssd_dims* d, const float* cs, void* states, float* final_state,
+                             hipStream_t stream) {
+    ssd_status st = ssd_check_dims(d);
+    if (st != SSD_OK) return st;
+    if (!final_state) return SSD_ERR_NULL_POINTER;
+    if (!aligned16(final_state)) return SSD_ERR_MISALIGNED;
+    ssd::Params p = make_params(d);
+    p.final_state = final_state;
+    if (d->batch == 0) return SSD_OK;
+    if (d->seqlen == 0)
+        return to_status(ssd::launch_zero_fill(final_state, d->batch * d->nheads * d->dstate * d->headdim, stream));
+    if (!cs || !states) return SSD_ERR_NULL_POINTER;
+    if (!aligned16(cs) || !aligned16(states)) return SSD_ERR_MISALIGNED;
+    p.cs = const_cast<float*>(cs);
+    p.states = states;
+    return to_status(ssd::launch_state_passing(p, d->state_dtype, stream));
+}
+
+ssd_status ssd_chunk_scan(const ssd_dims* d, const void* x, const float* dt, const void* B,
+                          const void* C, const float* D, const float* cs, const void* states,
+                          void* y, hipStream_t stream) {
+    ssd_status st = ssd_check_dims(d);
+    if (st != SSD_OK) return st;
+    if (empty(d)) return SSD_OK;
+    if (!x || !dt || !B || !C || !D || !cs || !states || !y) return SSD_ERR_NULL_POINTER;
+    if (!aligned16(x) || !aligned16(dt) || !aligned16(B) || !aligned16(C) || !aligned16(D) ||
+        !aligned16(cs) || !aligned16(states) || !aligned16(y))
+        return SSD_ERR_MISALIGNED;
+    ssd::Params p = make_params(d);
+    p.x = x;
+    p.dt = dt;
+    p.B = B;
+    p.C = C;
+    p.D = D;
+    p.cs = const_cast<float*>(cs);
+    p.states = const_cast<void*>(states);
+    p.y = y;
+    return to_status(ssd::launch_chunk_scan(p, d->dtype, d->state_dtype, stream));
+}
+
+ssd_status ssd_forward(const ssd_dims* d, const void* x, const float* dt, const float* A,
+                       const void* B, const void* C, const float* D, void* y,
+                       float* final_state, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+    ssd_status st = ssd_check_dims(d);
+    if (st != SSD_OK) return st;
+    if (d->batch == 0) return SSD_OK;
+    if (!final_state) return SSD_ERR_NULL_POINTER;
+    if (!aligned16(final_state)) return SSD_ERR_MISALIGNED;
+    if (d->seqlen == 0)
+        return to_status(ssd::launch_zero_fill(final_state, d->batch * d->nheads * d->dstate * d->headdim, stream));
+    if (!x || !dt || !A || !B || !C || !D || !y || !workspace) return SSD_ERR_NULL_POINTER;
+    if (!aligned16(x) || !aligned16(dt) || !aligned16(A) || !aligned16(B) || !aligned16(C) ||
+        !aligned16(D) || !aligned16(y) || !aligned16(workspace))
+        return SSD_ERR_MISALIGNED;
+    if (workspace_bytes < ssd_workspace_size(d)) return SSD_ERR_WORKSPACE_TOO_SMALL;
+    float* cs = static_cast<float*>(workspace);
+    void* states = static_cast<unsigned char*>(workspace) + round_up(cs_bytes_of(d));
+    st = ssd_chunk_cumsum(d, dt, A, cs, stream);
+    if (st == SSD_OK) st = ssd_chunk_state(d, x, dt, B, cs, states, stream);
+    if (st == SSD_OK) st = ssd_state_passing(d, cs, states, final_state, stream);
+    if (st == SSD_OK) st = ssd_chunk_scan(d, x, dt, B, C, D, cs, states, y, stream);
+    return st;
+}
+
+}  // extern "C"

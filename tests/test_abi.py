@@ -1,0 +1,148 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/ssd.h declares, and rejects bad arguments synchronously (before any
+HIP call, so these run on a machine without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mamba_ssd_scan_04_amd as ssd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssd.h")
+
+OK, NULLP, SHAPE, UNSUP, MISAL, WS = 0, 1, 2, 3, 4, 5
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ssd.LIB_PATH):
+        pytest.skip("libssd.so not built")
+    return ssd.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssd_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert {"ssd_forward", "ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_passing",
+            "ssd_chunk_scan", "ssd_workspace_size"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in ssd.h but not exported"
+
+
+def test_version_and_strings(lib):
+    assert ssd.ssd_abi_version() == 1
+    for code in range(7):
+        assert len(ssd.ssd_status_string(code)) > 0
+    assert "unknown" in ssd.ssd_status_string(99)
+
+
+def dims(**kw):
+    base = dict(batch=2, seqlen=512, nheads=8, headdim=64, dstate=128, ngroups=2,
+                chunk_size=256, dtype="bf16", state_dtype="fp32")
+    base.update(kw)
+    return ssd.make_dims(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({}, OK),
+    (dict(batch=0), OK),
+    (dict(seqlen=0), OK),
+    (dict(seqlen=1000), OK),
+    (dict(batch=-1), SHAPE),
+    (dict(seqlen=-5), SHAPE),
+    (dict(nheads=0), SHAPE),
+    (dict(ngroups=3), SHAPE),
+    (dict(chunk_size=0), SHAPE),
+    (dict(headdim=48), UNSUP),
+    (dict(headdim=256), UNSUP),
+    (dict(dstate=8), UNSUP),
+    (dict(dstate=512), UNSUP),
+    (dict(chunk_size=16), UNSUP),
+    (dict(chunk_size=100), UNSUP),
+    (dict(dtype=7), UNSUP),
+    (dict(state_dtype=5), UNSUP),
+    (dict(dtype="fp32", state_dtype="bf16"), UNSUP),
+    (dict(dtype="bf16", state_dtype="bf16"), OK),
+    (dict(dtype="fp32", headdim=16, dstate=16, chunk_size=64), OK),
+    (dict(dtype="fp32", headdim=128, dstate=256, chunk_size=256), UNSUP),  # fp32 tile > LDS
+    (dict(headdim=128, dstate=256, chunk_size=256), OK),
+])
+def test_check_dims(lib, kw, code):
+    assert ssd.ssd_check_dims(dims(**kw)) == code
+
+
+def test_check_dims_null(lib):
+    assert lib.ssd_check_dims(None) == NULLP
+    assert lib.ssd_workspace_size(None) == 0
+
+
+def test_workspace_size(lib):
+    d = dims()
+    nc = 2
+    cs = 2 * 8 * nc * 256 * 4
+    st = 2 * nc * 8 * 64 * 128 * 4
+    assert ssd.ssd_workspace_size(d) == cs + st
+    assert ssd.ssd_stage_sizes(d) == (cs, st)
+    assert ssd.ssd_workspace_size(dims(state_dtype="bf16")) == cs + st // 2
+    assert ssd.ssd_workspace_size(dims(headdim=48)) == 0
+    assert ssd.ssd_workspace_size(dims(batch=0)) == 0
+    # monotonic in every size
+    w = ssd.ssd_workspace_size(d)
+    for k, v in dict(batch=3, seqlen=513, nheads=10, headdim=128, dstate=256).items():
+        assert ssd.ssd_workspace_size(dims(**k and {k: v})) > w
+    # ragged T rounds up to whole chunks
+    assert ssd.ssd_workspace_size(dims(seqlen=300)) == ssd.ssd_workspace_size(dims(seqlen=512))
+
+
+def _fake(addr):
+    return ctypes.c_void_p(addr)
+
+
+def test_forward_argument_errors(lib):
+    d = dims()
+    ws = ssd.ssd_workspace_size(d)
+    good = [_fake(0x100000 * (i + 1)) for i in range(10)]
+    x, dt, A, B, C, D, y, fin, work = good[:9]
+    f = lib.ssd_forward
+    P = ctypes.byref
+    assert f(P(d), None, dt, A, B, C, D, y, fin, work, ws, None) == NULLP
+    assert f(P(d), x, dt, A, B, C, D, y, None, work, ws, None) == NULLP
+    assert f(P(d), x, dt, A, B, C, D, y, fin, None, ws, None) == NULLP
+    assert f(P(d), _fake(0x100008), dt, A, B, C, D, y, fin, work, ws, None) == MISAL
+    assert f(P(d), x, dt, A, B, C, D, y, _fake(0x100004), work, ws, None) == MISAL
+    assert f(P(d), x, dt, A, B, C, D, y, fin, work, ws - 1, None) == WS
+    bad = dims(ngroups=3)
+    assert f(P(bad), x, dt, A, B, C, D, y, fin, work, ws, None) == SHAPE
+    # batch == 0 is a no-op that succeeds without touching any pointer
+    assert f(P(dims(batch=0)), None, None, None, None, None, None, None, None, None, 0, None) == OK
+
+
+def test_stage_argument_errors(lib):
+    d = dims()
+    P = ctypes.byref
+    a = _fake(0x200000)
+    assert lib.ssd_chunk_cumsum(P(d), None, a, a, None) == NULLP
+    assert lib.ssd_chunk_cumsum(P(d), a, a, _fake(0x200002), None) == MISAL
+    assert lib.ssd_chunk_state(P(d), a, a, a, a, None, None) == NULLP
+    assert lib.ssd_state_passing(P(d), a, a, None, None) == NULLP
+    assert lib.ssd_chunk_scan(P(d), a, a, a, a, a, a, a, None, None) == NULLP
+    assert lib.ssd_chunk_scan(P(dims(headdim=40)), a, a, a, a, a, a, a, a, None) == UNSUP
+    # empty inputs: nothing to do, success without pointers
+    e = dims(seqlen=0)
+    assert lib.ssd_chunk_cumsum(P(e), None, None, None, None) == OK
+    assert lib.ssd_chunk_state(P(e), None, None, None, None, None, None) == OK
+    assert lib.ssd_chunk_scan(P(e), None, None, None, None, None, None, None, None, None) == OK
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(ssd, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(ssd, "_lib", None)
+    with pytest.raises(RuntimeError, match="not found"):
+        ssd.load_library()

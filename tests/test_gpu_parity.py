@@ -1,0 +1,162 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Sizes here are ones the oracle finishes in seconds but that still span several
+32-row tiles, several chunks and a ragged last chunk. Full-size workloads are
+checked on sampled (batch, head) pairs in test_gpu_fullsize.py.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mamba_ssd_scan_04_amd as ssd
+import oracle
+from mamba_ssd_scan_04_amd import inputs
+from gpu_helpers import TOL, gpu_forward, oracle_forward, say, to_dev, workload
+
+pytestmark = pytest.mark.gpu
+
+
+def check(w, inp, state_dtype="fp32", tol=None):
+    say(f"case {w.describe()} state={state_dtype}")
+    y, fin = gpu_forward(inp, w.chunk_size, state_dtype)
+    y_ref, fin_ref = oracle_forward(inp)
+    ey, ef = oracle.rel_err(y, y_ref), oracle.rel_err(fin, fin_ref)
+    say(f"  err_y={ey:.3e} err_final={ef:.3e}")
+    t = tol or TOL[w.dtype]
+    assert np.all(np.isfinite(y)) and np.all(np.isfinite(fin))
+    assert ey <= t, f"y error {ey} > {t}"
+    assert ef <= t, f"final state error {ef} > {t}"
+    return ey, ef
+
+
+def test_tiny_fp32_full():
+    """The tiny fp32 workload at its full size: b1 T256 H2 P16 N16 Q64."""
+    w = workload("tiny")
+    check(w, inputs.generate(w))
+
+
+@pytest.mark.parametrize("state_dtype", ["fp32", "bf16"])
+def test_m125_shape_ragged(state_dtype):
+    """125M-layer head shape (P64 N128 Q256) with a ragged last chunk (T=1000)."""
+    w = workload("m125", batch=2, seqlen=1000, nheads=4)
+    check(w, inputs.generate(w, seed=1), state_dtype)
+
+
+@pytest.mark.parametrize("state_dtype", ["fp32", "bf16"])
+def test_slow_decay_inter_chunk_path(state_dtype):
+    """|A| in [1e-3, 1e-1]: the state carried between chunks dominates y."""
+    w = workload("m125", batch=1, seqlen=1024, nheads=3)
+    check(w, inputs.generate_slow_decay(w, seed=2), state_dtype)
+
+
+@pytest.mark.parametrize("Q", [32, 64, 128, 256])
+def test_chunk_sizes(Q):
+    w = workload("m125", batch=1, seqlen=600, nheads=2, chunk_size=Q)
+    check(w, inputs.generate_slow_decay(w, seed=3))
+
+
+@pytest.mark.parametrize("P,N", [(16, 16), (32, 64), (64, 16), (64, 256), (128, 128), (128, 256), (16, 256)])
+def test_head_and_state_dims(P, N):
+    w = workload("m125", batch=1, seqlen=520, nheads=3, headdim=P, dstate=N)
+    check(w, inputs.generate_slow_decay(w, seed=4))
+
+
+@pytest.mark.parametrize("H,G", [(6, 2), (6, 6), (24, 8)])
+def test_group_patterns(H, G):
+    """Knowl 7: multi-input (G=1, other tests), grouped (1<G<H) and multi-head (G=H)."""
+    w = workload("m125", batch=2, seqlen=300, nheads=H, ngroups=G)
+    check(w, inputs.generate_slow_decay(w, seed=5))
+
+
+@pytest.mark.parametrize("P,N,Q", [(16, 16, 64), (64, 128, 128), (32, 32, 32), (64, 64, 256)])
+def test_fp32_inputs(P, N, Q):
+    w = workload("tiny", batch=2, seqlen=333, nheads=3, headdim=P, dstate=N, chunk_size=Q)
+    check(w, inputs.generate_slow_decay(w, seed=6))
+
+
+@pytest.mark.parametrize("T", [1, 31, 32, 33, 255, 257])
+def test_short_and_boundary_lengths(T):
+    w = workload("m125", batch=2, seqlen=T, nheads=2)
+    check(w, inputs.generate_slow_decay(w, seed=7))
+
+
+def test_no_decay_linear_attention():
+    """A = 0 (a = 1 everywhere): nothing decays, every path carries full weight."""
+    w = workload("m125", batch=1, seqlen=700, nheads=2)
+    inp = inputs.generate(w, seed=8)
+    inp["A"] = torch.zeros_like(inp["A"])
+    check(w, inp)
+
+
+def test_full_decay_memoryless():
+    """dt*A <= -800: a = 0, y_t = dt_t (C_t.B_t) x_t + D x_t."""
+    w = workload("tiny", batch=1, seqlen=200, nheads=2)
+    inp = inputs.generate(w, seed=9)
+    inp["dt"] = torch.full_like(inp["dt"], 50.0)
+    inp["A"] = torch.full_like(inp["A"], -20.0)
+    check(w, inp)
+
+
+def test_empty_inputs():
+    w = workload("m125", batch=2, seqlen=64, nheads=2)
+    inp = to_dev(inputs.generate(w))
+    # seqlen 0: final state is zero, nothing else touched
+    x0 = inp["x"][:, :0].contiguous()
+    B0 = inp["B"][:, :0].contiguous()
+    y, fin = ssd.forward(x0, inp["dt"][:, :0].contiguous(), inp["A"], B0, inp["C"][:, :0].contiguous(),
+                         inp["D"], 256)
+    torch.cuda.synchronize()
+    assert y.numel() == 0 and torch.all(fin == 0)
+    # batch 0
+    y, fin = ssd.forward(inp["x"][:0], inp["dt"][:0], inp["A"], inp["B"][:0], inp["C"][:0], inp["D"], 256)
+    torch.cuda.synchronize()
+    assert y.numel() == 0 and fin.numel() == 0
+
+
+def test_deterministic_and_fully_written():
+    """Two runs agree bitwise, and no output or intermediate is left unwritten
+    (outputs and workspace prefilled with NaN)."""
+    w = workload("m125", batch=2, seqlen=777, nheads=4)
+    inp = to_dev(inputs.generate(w, seed=10))
+    d = ssd.dims_of(inp["x"], inp["B"], w.chunk_size)
+    outs = []
+    for _ in range(2):
+        ws = torch.full((ssd.ssd_workspace_size(d),), 255, dtype=torch.uint8, device="cuda")
+        y = torch.full_like(inp["x"], float("nan"))
+        fin = torch.full((w.batch, w.nheads, w.dstate, w.headdim), float("nan"), device="cuda")
+        ssd.ssd_forward(d, inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], y, fin, ws,
+                        ws.numel())
+        torch.cuda.synchronize()
+        assert torch.isfinite(y.float()).all() and torch.isfinite(fin).all()
+        outs.append((y.clone(), fin.clone()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+@pytest.mark.parametrize("state_dtype", ["fp32", "bf16"])
+def test_stage_parity(state_dtype):
+    """Each stage against its fp64 counterpart: cs against the block algorithm's
+    prefix sums, S against its chunk states, h_in against the recurrence's state
+    at every chunk boundary, final and y against the recurrence."""
+    w = workload("m125", batch=2, seqlen=900, nheads=3, ngroups=1)
+    inp = inputs.generate_slow_decay(w, seed=11)
+    say(f"stage case {w.describe()} state={state_dtype}")
+    dev = to_dev(inp)
+    out = ssd.stages(dev["x"], dev["dt"], dev["A"], dev["B"], dev["C"], dev["D"], w.chunk_size, state_dtype)
+    torch.cuda.synchronize()
+    f = inputs.to_float64(inp)
+    ref = oracle.chunked(f["x"], f["dt"], f["A"], f["B"], f["C"], f["D"], Q=w.chunk_size)
+    y_ref, fin_ref, snaps = oracle.recurrence(f["x"], f["dt"], f["A"], f["B"], f["C"], f["D"],
+                                              snap_every=w.chunk_size)
+    cs = out["cs"].cpu().numpy().astype(np.float64)
+    valid = ~np.isnan(ref["cs"])
+    assert oracle.rel_err(cs[valid], ref["cs"][valid]) < 1e-5
+    # padding positions of the ragged chunk repeat the chunk's last value
+    last = w.seqlen - (w.nchunks - 1) * w.chunk_size
+    assert np.all(cs[:, :, -1, last:] == cs[:, :, -1, last - 1: last])
+    tol = TOL[w.dtype]
+    S = out["S"].float().cpu().numpy().astype(np.float64).transpose(0, 1, 2, 4, 3)   # -> [b,nc,H,N,P]
+    assert oracle.rel_err(S, ref["S"]) < tol
+    h_in = out["h_in"].float().cpu().numpy().astype(np.float64).transpose(0, 1, 2, 4, 3)
+    assert oracle.rel_err(h_in, snaps) < tol
+    assert oracle.rel_err(out["final"].cpu().numpy(), fin_ref) < tol
+    assert oracle.rel_err(out["y"].float().cpu().numpy(), y_ref) < tol
