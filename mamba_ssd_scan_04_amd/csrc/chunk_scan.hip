@@ -9,206 +9,379 @@
 //
 //   y_j = sum_{i<=j} (C_j . B_i) exp(cs_j - cs_i) dt_i x_i  +  exp(cs_j) C_j^T h_c  +  D x_j
 //
-// Matrix-core mapping. Row tiles of 32 tokens j; key tiles of 32 tokens i.
-//  1. M^T tile = B_i-tile . C_j-tile^T over n (both operands read straight
-//     from memory: B and C rows are n-contiguous). Its accumulator gives each
-//     lane one column j and 16 rows i.
-//  2. The lane scales its 16 values by exp(cs_j - cs_i) dt_i (masking i > j),
-//     rounds them to the operand type, and uses them directly as the A operand
-//     (row j, 8 values of k = i per lane half) of Y += M . X. The k order this
-//     induces is matched by storing x^T in LDS in "fragment order"
-//     (frag_token), so no data moves between lanes.
-//  3. Y += (exp(cs_j) C_j) . h_c, with h_c staged in LDS ([P][N], k-major).
-//  4. Epilogue adds D x_j (x read back from the LDS tile) and stores y.
-// The accumulator of Y holds column p = lane%32 and 16 rows j per lane.
-//
-// Grid: (chunk, head, batch), 256 threads = 4 wavefronts. With 8 row tiles,
-// wavefront w takes tiles w and 7 - w so the causal work (rt + 1 key tiles
-// per row tile) is balanced.
+// Work split. One workgroup of 8 wavefronts takes one chunk and `hpw` heads of
+// one group; wavefront w owns the 32-token row tile w (rows j), for every head.
+//  Phase A, once per workgroup: C B^T does not depend on the head when B and C
+//  are shared (Knowl 7), so each wavefront computes its row of 32x32 tiles
+//  M^T(kt) = B_kt . C_w^T (kt <= w) on the matrix cores, rounds them to the
+//  operand type and keeps them in registers, together with its C rows.
+//  Phase B, per head: x (token-major) and h_c ([P][N]) are copied into LDS by
+//  global_load_lds, double-buffered so the next head's copy overlaps this
+//  head's math. For every key tile the lane scales its 16 register values by
+//  the decay (exp(cs_j - cs_r) * exp(cs_r - cs_i) dt_i with r the key tile's
+//  last token off the diagonal; a direct exp with the causal mask on it) and
+//  feeds them straight to Y += M . X as the A operand: an accumulator's rows
+//  (8g + 4hf + r) become the next product's k index in "fragment order", and
+//  the x fragment is read from LDS with transpose reads in the same order.
+//  The carried-state term is (C . h_c) with rows scaled by exp(cs_j).
+//  The epilogue adds D x_j and stores y (lane = column p).
 #include "kernels.hpp"
-#include "transpose.hpp"
 
 namespace ssd {
 
 constexpr int kScanMaxLds = 160 * 1024;
-
-template <typename T> constexpr int pad_elems() { return 16 / (int)sizeof(T); }
-
-template <typename T, int PT, int NT>
-__host__ __device__ constexpr int scan_ldh() { return NT * 32 + pad_elems<T>(); }
-
-// Dynamic LDS bytes of the chunk scan for chunk size Q.
-template <typename T, int PT, int NT>
-__host__ __device__ inline int scan_lds_bytes(int Q) {
-    return PT * 32 * (Q + pad_elems<T>()) * (int)sizeof(T) + PT * 32 * scan_ldh<T, PT, NT>() * (int)sizeof(T) +
-           2 * Q * (int)sizeof(float);
-}
-
-template <typename T>
-__device__ __forceinline__ typename Vec8<T>::type scale8(const typename Vec8<T>::type& v, float s) {
-    typename Vec8<T>::type o;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = from_f32<T>(to_f32(v[e]) * s);
-    return o;
-}
+constexpr int kScanThreads = 256;
 
 template <typename T, int PT, int NT, typename ST>
-__global__ __launch_bounds__(256) void ssd_chunk_scan_kernel(Params p) {
-    constexpr int PP = PT * 32, NP = NT * 32, KS = NP / 16;
-    constexpr int LDH = scan_ldh<T, PT, NT>();
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    const int Q = (int)p.chunk;
-    const int LDX = Q + pad_elems<T>();
-    T* xs = reinterpret_cast<T*>(smem);                 // [PP][LDX]  x^T, fragment order
-    T* hs = xs + PP * LDX;                              // [PP][LDH]  h_c^T
-    float* c2s = reinterpret_cast<float*>(hs + PP * LDH);  // [Q] cs * log2(e)
-    float* dts = c2s + Q;                               // [Q] dt (0 past the end)
+struct ScanCfg {
+    static constexpr int EPC = 16 / (int)sizeof(T);
+    static constexpr int XRC = PT * 32 / EPC;                  // chunks per x row
+    static constexpr int HRC = NT * 32 * (int)sizeof(ST) / 16; // chunks per h_c row
+    static constexpr int HBYTES = PT * 32 * HRC * 16;          // one head's h_c tile
+    static constexpr int KS = NT * 2;                          // k16 steps over n
+    __host__ __device__ static int xbytes(int Q) { return Q * XRC * 16; }
+    __host__ __device__ static int vbytes(int Q) { return 4 * Q * 4; }
+    // bytes of LDS with nbx x buffers and nbh h_c buffers
+    __host__ __device__ static int lds(int Q, int nbx, int nbh) { return nbx * xbytes(Q) + nbh * HBYTES + 2 * vbytes(Q); }
+};
 
-    const int c = blockIdx.x;
-    const int64_t h = blockIdx.y, b = blockIdx.z;
-    const int64_t T_ = p.seqlen, H = p.nheads, P = p.headdim, N = p.dstate, G = p.ngroups;
-    const int64_t g = h / p.heads_per_group;
-    const int64_t t0 = (int64_t)c * Q;
-    const T* xg = static_cast<const T*>(p.x);
-    const T* bg = static_cast<const T*>(p.B);
-    const T* cg = static_cast<const T*>(p.C);
+// Per-head LDS views used by one row tile's math.
+template <typename T, typename ST>
+struct HeadView {
+    const T* xt;      // x tile, token-major, swizzled
+    const ST* ht;     // h_c^T tile [P][N], swizzled
+    const float* c2;  // cs * log2(e)
+    const float* dt;  // dt (0 past the end)
+    const float* ecs; // exp(cs)
+    const float* u;   // exp(cs_r - cs_i) dt_i, r = the 32-token tile's last token
+};
 
-    const float* csrow = p.cs + ((b * H + h) * p.nchunks + c) * Q;
-    for (int j = threadIdx.x; j < Q; j += blockDim.x) {
-        const int64_t t = t0 + j;
-        c2s[j] = csrow[j] * kLog2e;
-        dts[j] = (t < T_) ? p.dt[(b * T_ + t) * H + h] : 0.0f;
-    }
-    // x^T in fragment order: block m covers LDS positions [8m, 8m+8) of a row
-    for (int sb = threadIdx.x; sb < (Q / 8) * (PP / 8); sb += blockDim.x) {
-        const int col = (sb % (PP / 8)) * 8, m = sb / (PP / 8);
-        float v[8][8];
+// C B^T row of tiles for row tile rt: key tiles kt < rt into cb[kt], the
+// diagonal tile kt == rt into cbd; rows past qc and columns past N are zero.
+// B fragments for key tile kt+1 are loaded while tile kt is multiplied.
+template <typename T, int KS, int SLOTS>
+__device__ __forceinline__ void cb_row(typename Vec8<T>::type (&cb)[SLOTS][2], typename Vec8<T>::type (&cbd)[2],
+                                       const typename Vec8<T>::type (&creg)[KS], const T* bbase, uint32_t bcs,
+                                       int rt, int qc, int N, int l32, int hf) {
+    using V8 = typename Vec8<T>::type;
+    const int nlast = N - 8;
+    auto off = [&](int row, int ks) {
+        return (uint32_t)min(row, qc - 1) * bcs + (uint32_t)min(ks * 16 + hf * 8, nlast);
+    };
+    V8 bnext[KS];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int q = 8 * m + e;
-            const int j = (q & ~15) + frag_token(q & 15);
-            const int64_t t = t0 + j;
-            load_row8<T>(v[e], xg + ((b * T_ + t) * H + h) * P + col, (t < T_) && (col < P));
-        }
-        store_transposed8<T>(xs + col * LDX + 8 * m, LDX, v);
-    }
-    if (c > 0) {
-        const ST* sg = static_cast<const ST*>(p.states) + ((b * p.nchunks + c) * H + h) * P * N;
-        for (int it = threadIdx.x; it < PP * (NP / 8); it += blockDim.x) {
-            const int pr = it / (NP / 8), n0 = (it % (NP / 8)) * 8;
-            float v[8];
-            load_row8<ST>(v, sg + pr * N + n0, (pr < P) && (n0 < N));
-            typename Vec8<T>::type o;
+    for (int ks = 0; ks < KS; ++ks) bnext[ks] = ldg8(bbase + off(l32, ks));
 #pragma unroll
-            for (int e = 0; e < 8; ++e) o[e] = from_f32<T>(v[e]);
-            store8(hs + pr * LDH + n0, o);
+    for (int kt = 0; kt <= SLOTS; ++kt) {
+        if (kt <= rt) {
+            V8 bcur[KS];
+            const bool rok = kt * 32 + l32 < qc;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) bcur[ks] = (rok && ks * 16 + hf * 8 < N) ? bnext[ks] : zero8<T>();
+            if (kt < rt) {
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) bnext[ks] = ldg8(bbase + off((kt + 1) * 32 + l32, ks));
+            }
+            f32x16 acc = zero16();
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) mma_k16(acc, bcur[ks], creg[ks]);
+            V8 lo, hi;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                lo[e] = from_f32<T>(acc[e]);
+                hi[e] = from_f32<T>(acc[8 + e]);
+            }
+            if (kt < rt) {
+                cb[kt < SLOTS ? kt : SLOTS - 1][0] = lo;
+                cb[kt < SLOTS ? kt : SLOTS - 1][1] = hi;
+            } else {
+                cbd[0] = lo;
+                cbd[1] = hi;
+            }
         }
     }
-    __syncthreads();
+}
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// One head's output for row tile rt: (C . h_c) scaled by exp(cs_j), plus the
+// decayed, masked C B^T tiles times x, plus D x; stores y. rt, qc and P arrive
+// through an empty asm so per-element compares stay inside the head loop
+// instead of being hoisted (as lane masks) across it.
+template <typename T, int PT, int KS, int XRC, int HRC, int SLOTS, typename ST>
+__device__ __forceinline__ void row_tile_head(const typename Vec8<T>::type (&cb)[SLOTS][2],
+                                              const typename Vec8<T>::type (&cbd)[2],
+                                              const typename Vec8<T>::type (&creg)[KS], const HeadView<T, ST>& v,
+                                              int rt, bool carried, float Dh, T* yh, uint32_t ystride, int qc,
+                                              int P, int lane) {
+    using V8 = typename Vec8<T>::type;
     const int hf = lane >> 5, l32 = lane & 31;
-    const int RT = Q / 32;
-    int tiles[2] = {-1, -1};
-    if (RT == 8) {
-        tiles[0] = wave;
-        tiles[1] = 7 - wave;
-    } else if (wave < RT) {
-        tiles[0] = wave;
+    int jl = rt * 32 + l32;
+    asm volatile("" : "+v"(jl), "+v"(qc), "+v"(P));
+    f32x16 acc[PT];
+#pragma unroll
+    for (int pt = 0; pt < PT; ++pt) acc[pt] = zero16();
+    if (carried) {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt)
+                mma_k16(acc[pt], creg[ks], cvt8<T>(row8<HRC>(v.ht, pt * 32 + l32, ks * 16 + hf * 8)));
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+            const f32x4 e4 = *reinterpret_cast<const f32x4*>(v.ecs + rt * 32 + 8 * gq + 4 * hf);
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc[pt][4 * gq + r] *= e4[r];
+        }
     }
-    const float Dh = p.D[h];
-    T* yg = static_cast<T*>(p.y);
-
-    for (int ti = 0; ti < 2; ++ti) {
-        const int rt = tiles[ti];
-        if (rt < 0) continue;
-        const int jl = rt * 32 + l32;            // this lane's row j (as MFMA column / A row)
-        const int64_t tj = t0 + jl;
-        typename Vec8<T>::type creg[KS];
+    const float c2j = v.c2[jl];
+    // key tiles off the diagonal: M = CB * exp(cs_j - cs_r) * u_i, no mask
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const int n0 = ks * 16 + hf * 8;
-            creg[ks] = (tj < T_ && n0 < N) ? load8(cg + ((b * T_ + tj) * G + g) * N + n0) : zero8<T>();
-        }
-        f32x16 acc[PT];
+    for (int kt = 0; kt < SLOTS; ++kt) {
+        if (kt < rt) {
+            const float vj = exp2f(c2j - v.c2[kt * 32 + 31]);
+            V8 aop[2];
 #pragma unroll
-        for (int pt = 0; pt < PT; ++pt) acc[pt] = zero16();
-        const float c2j = c2s[jl];
-
-        if (c > 0) {  // off-diagonal term: (exp(cs_j) C_j) . h_c
-            const float sj = exp2f(c2j);
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const auto a = scale8<T>(creg[ks], sj);
-#pragma unroll
-                for (int pt = 0; pt < PT; ++pt)
-                    mma_k16(acc[pt], a, load8(hs + (pt * 32 + l32) * LDH + ks * 16 + hf * 8));
-            }
-        }
-
-        for (int kt = 0; kt <= rt; ++kt) {
-            const int il = kt * 32 + l32;
-            const int64_t ti_ = t0 + il;
-            f32x16 cb = zero16();
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int n0 = ks * 16 + hf * 8;
-                const auto bop = (ti_ < T_ && n0 < N) ? load8(bg + ((b * T_ + ti_) * G + g) * N + n0) : zero8<T>();
-                mma_k16(cb, bop, creg[ks]);
-            }
-            // cb[r]: row i = kt*32 + 8*(r/4) + 4*hf + r%4, column j = jl
-            typename Vec8<T>::type aop[2];
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const int ib = kt * 32 + 8 * q4 + 4 * hf;
-                const f32x4 ci = *reinterpret_cast<const f32x4*>(c2s + ib);
-                const f32x4 di = *reinterpret_cast<const f32x4*>(dts + ib);
+            for (int gq = 0; gq < 4; ++gq) {
+                const f32x4 u4 = *reinterpret_cast<const f32x4*>(v.u + kt * 32 + 8 * gq + 4 * hf);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    float v = cb[4 * q4 + r] * exp2f(c2j - ci[r]) * di[r];
-                    v = (ib + r <= jl) ? v : 0.0f;
-                    aop[q4 >> 1][4 * (q4 & 1) + r] = from_f32<T>(v);
+                    const int idx = 4 * gq + r;
+                    aop[idx >> 3][idx & 7] = from_f32<T>(to_f32(cb[kt][idx >> 3][idx & 7]) * vj * u4[r]);
                 }
             }
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
+                auto rowk = [kt, s](int hf_, int e) { return kt * 32 + 16 * s + 8 * (e >> 2) + 4 * hf_ + (e & 3); };
 #pragma unroll
-                for (int pt = 0; pt < PT; ++pt)
-                    mma_k16(acc[pt], aop[s], load8(xs + (pt * 32 + l32) * LDX + (kt * 2 + s) * 16 + hf * 8));
-            }
-        }
-
-        // epilogue: + D x_j, store y
-#pragma unroll
-        for (int pt = 0; pt < PT; ++pt) {
-            const int pc = pt * 32 + l32;
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const auto xv = load8(xs + pc * LDX + (rt * 2 + s) * 16 + hf * 8);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int r = 8 * s + e;
-                    const int j = rt * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-                    const int64_t t = t0 + j;
-                    if (t < T_ && pc < P)
-                        yg[((b * T_ + t) * H + h) * P + pc] = from_f32<T>(acc[pt][r] + Dh * to_f32(xv[e]));
-                }
+                for (int pt = 0; pt < PT; ++pt) mma_k16(acc[pt], aop[s], frag_tr<XRC>(v.xt, pt * 32, rowk, lane));
             }
         }
     }
+    // the diagonal tile: direct decay; the causal mask (i <= j) enters as a
+    // -inf exponent for i > j, so exp2 gives exactly 0 with no lane masks
+    {
+        V8 aop[2];
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+            const int ib = rt * 32 + 8 * gq + 4 * hf;
+            const f32x4 ci = *reinterpret_cast<const f32x4*>(v.c2 + ib);
+            const f32x4 di = *reinterpret_cast<const f32x4*>(v.dt + ib);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int idx = 4 * gq + r;
+                const float pen = __int_as_float(((jl - (ib + r)) >> 31) & (int)0xff800000u);
+                const float m = to_f32(cbd[idx >> 3][idx & 7]) * exp2f((c2j - ci[r]) + pen) * di[r];
+                aop[idx >> 3][idx & 7] = from_f32<T>(m);
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            auto rowk = [rt, s](int hf_, int e) { return rt * 32 + 16 * s + 8 * (e >> 2) + 4 * hf_ + (e & 3); };
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) mma_k16(acc[pt], aop[s], frag_tr<XRC>(v.xt, pt * 32, rowk, lane));
+        }
+    }
+    // epilogue: + D x_j (the diagonal tile's x fragments have the accumulator's rows)
+#pragma unroll
+    for (int pt = 0; pt < PT; ++pt) {
+        const int pc = pt * 32 + l32;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            auto rowk = [rt, s](int hf_, int e) { return rt * 32 + 16 * s + 8 * (e >> 2) + 4 * hf_ + (e & 3); };
+            const V8 xd = frag_tr<XRC>(v.xt, pt * 32, rowk, lane);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int r = 8 * s + e;
+                const int j = rt * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+                if (j < qc && pc < P)
+                    stg<T>(yh + (uint32_t)j * ystride + pc, from_f32<T>(acc[pt][r] + Dh * to_f32(xd[e])));
+            }
+        }
+    }
+}
+
+template <typename T, int PT, int NT, typename ST, int NBX, int NBH>
+__global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void ssd_chunk_scan_kernel(Params p, int hpw) {
+    using Cfg = ScanCfg<T, PT, NT, ST>;
+    using V8 = typename Vec8<T>::type;
+    constexpr int KS = Cfg::KS;
+    constexpr int ESZ = (int)sizeof(T), SSZ = (int)sizeof(ST);
+    extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+    const int Q = (int)p.chunk;
+    const int XB = Cfg::xbytes(Q), VB = Cfg::vbytes(Q);
+    unsigned char* const hb0 = smem + NBX * XB;
+    float* const vb0 = reinterpret_cast<float*>(hb0 + NBH * Cfg::HBYTES);
+
+    // ---- block coordinates (uniform) ----
+    const int64_t T_ = p.seqlen, H = p.nheads, P = p.headdim, N = p.dstate, G = p.ngroups;
+    const int64_t hpg = p.heads_per_group, nc = p.nchunks;
+    const int nhb = (int)((hpg + hpw - 1) / hpw);
+    int bx = blockIdx.x;
+    const int hb = bx % nhb;
+    bx /= nhb;
+    const int64_t g = bx % G;
+    const int c = (int)(bx / G);
+    const int64_t b = blockIdx.y;
+    const int64_t h0 = g * hpg + (int64_t)hb * hpw;
+    const int nh = (int)min<int64_t>(hpw, hpg - (int64_t)hb * hpw);
+    const int64_t t0 = (int64_t)c * Q;
+    const int qc = (int)min<int64_t>(Q, T_ - t0);
+    const int64_t tok0 = b * T_ + t0;            // first token row of the chunk
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int hf = lane >> 5, l32 = lane & 31;
+    // row tiles of this wavefront: with 8 tiles, w and 7 - w (causal work
+    // (rt + 1) + (8 - rt) = 9 key tiles each); with fewer, tile w alone
+    const int RT = Q / 32;
+    const int rs = wave < RT ? wave : -1;                 // short row (<= 3 when RT == 8)
+    const int rl = RT == 8 ? 7 - wave : -1;               // long row (>= 4)
+
+    const uint32_t bcs = (uint32_t)(G * N);
+    const T* cbase = static_cast<const T*>(p.C) + (tok0 * G + g) * N;
+    const T* bbase = static_cast<const T*>(p.B) + (tok0 * G + g) * N;
+    const unsigned char* xbase = static_cast<const unsigned char*>(p.x) + (tok0 * H + h0) * P * ESZ;
+    const uint32_t xstride = (uint32_t)(H * P * ESZ);
+    const unsigned char* sbase = static_cast<const unsigned char*>(p.states) + ((b * nc + c) * H + h0) * P * N * SSZ;
+    T* ybase = static_cast<T*>(p.y) + (tok0 * H + h0) * P;
+    const uint32_t ystride = (uint32_t)(H * P);
+    const float* csbase = p.cs + ((b * H + h0) * nc + c) * Q;
+    const float* dtbase = p.dt + tok0 * H + h0;
+    const int xvalid = (int)(P * ESZ / 16), hvalid = (int)(N * SSZ / 16);
+
+    auto issue_x = [&](int hh, int buf) {
+        dma_tile<Cfg::XRC>(smem + buf * XB, Q, qc, xvalid, xbase + (int64_t)hh * P * ESZ, xstride, wave,
+                           kScanThreads / 64, lane);
+    };
+    auto issue_h = [&](int hh, int buf) {
+        dma_tile<Cfg::HRC>(hb0 + buf * Cfg::HBYTES, PT * 32, (int)P, hvalid, sbase + (int64_t)hh * P * N * SSZ,
+                           (uint32_t)(N * SSZ), wave, kScanThreads / 64, lane);
+    };
+    float vcs = 0.0f, vcr = 0.0f, vdt = 0.0f;   // thread i holds token i of the next head
+    auto load_vec = [&](int hh) {
+        const int i = threadIdx.x;
+        if (i < Q) {
+            const float* csr = csbase + (int64_t)hh * nc * Q;
+            vcs = ldg(csr + i);
+            vcr = ldg(csr + (i | 31));
+            vdt = (i < qc) ? ldg(dtbase + hh + (uint32_t)i * (uint32_t)H) : 0.0f;
+        }
+    };
+    auto store_vec = [&](int buf) {
+        const int i = threadIdx.x;
+        if (i < Q) {
+            float* v = vb0 + buf * (VB / 4);
+            const float c2 = vcs * kLog2e, c2r = vcr * kLog2e;
+            v[i] = c2;
+            v[Q + i] = vdt;
+            v[2 * Q + i] = exp2f(c2);
+            v[3 * Q + i] = exp2f(c2r - c2) * vdt;
+        }
+    };
+
+    // head 0's tiles start moving before phase A
+    if (nh > 0) {
+        issue_x(0, 0);
+        if (c > 0) issue_h(0, 0);
+        load_vec(0);
+    }
+
+    // ---- phase A: C rows and C B^T rows of tiles, once per workgroup ----
+    const int nlast = (int)N - 8;
+    V8 cs_reg[KS], cl_reg[KS];        // C rows of the short / long row tile
+    V8 cb_s[3][2], cb_l[7][2];        // their C B^T tiles off the diagonal (kt < rt)
+    V8 cbd_s[2], cbd_l[2];            // and on it
+    auto load_c = [&](V8 (&cr)[KS], int rt) {
+        const int j = rt * 32 + l32;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const V8 raw = ldg8(cbase + (uint32_t)min(j, qc - 1) * bcs + (uint32_t)min(ks * 16 + hf * 8, nlast));
+            cr[ks] = (j < qc && ks * 16 + hf * 8 < (int)N) ? raw : zero8<T>();
+        }
+    };
+    if (rs >= 0) {
+        load_c(cs_reg, rs);
+        cb_row<T, KS, 3>(cb_s, cbd_s, cs_reg, bbase, bcs, rs, qc, (int)N, l32, hf);
+    }
+    if (rl >= 0) {
+        load_c(cl_reg, rl);
+        cb_row<T, KS, 7>(cb_l, cbd_l, cl_reg, bbase, bcs, rl, qc, (int)N, l32, hf);
+    }
+    if (nh > 0) store_vec(0);
+    wait_vmem();
+    __syncthreads();
+
+    // ---- phase B: heads ----
+    for (int hh = 0; hh < nh; ++hh) {
+        const int buf = hh & 1;
+        const int xbi = NBX == 2 ? buf : 0;
+        const int hbi = NBH == 2 ? buf : 0;
+        const bool more = hh + 1 < nh;
+        if (more) {
+            if (NBX == 2) issue_x(hh + 1, buf ^ 1);
+            if (NBH == 2 && c > 0) issue_h(hh + 1, buf ^ 1);
+            load_vec(hh + 1);
+        }
+        HeadView<T, ST> v;
+        v.xt = reinterpret_cast<const T*>(smem + xbi * XB);
+        v.ht = reinterpret_cast<const ST*>(hb0 + hbi * Cfg::HBYTES);
+        v.c2 = vb0 + buf * (VB / 4);
+        v.dt = v.c2 + Q;
+        v.ecs = v.c2 + 2 * Q;
+        v.u = v.c2 + 3 * Q;
+        const float Dh = ldg(p.D + h0 + hh);
+        T* yh = ybase + (int64_t)hh * P;
+        if (rs >= 0)
+            row_tile_head<T, PT, KS, Cfg::XRC, Cfg::HRC, 3, ST>(cb_s, cbd_s, cs_reg, v, rs, c > 0, Dh, yh, ystride, qc,
+                                                                (int)P, lane);
+        if (rl >= 0)
+            row_tile_head<T, PT, KS, Cfg::XRC, Cfg::HRC, 7, ST>(cb_l, cbd_l, cl_reg, v, rl, c > 0, Dh, yh, ystride, qc,
+                                                                (int)P, lane);
+        if (more) store_vec(buf ^ 1);
+        wait_vmem();
+        __syncthreads();
+        if (more && (NBX == 1 || (NBH == 1 && c > 0))) {   // single-buffered tiles
+            if (NBX == 1) issue_x(hh + 1, 0);
+            if (NBH == 1 && c > 0) issue_h(hh + 1, 0);
+            wait_vmem();
+            __syncthreads();
+        }
+    }
+}
+
+template <typename T, int PT, int NT, typename ST, int NBX, int NBH>
+static hipError_t launch_sc2(const Params& p, int hpw, int lds, hipStream_t s) {
+    auto kern = ssd_chunk_scan_kernel<T, PT, NT, ST, NBX, NBH>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    const int64_t nhb = (p.heads_per_group + hpw - 1) / hpw;
+    dim3 grid((unsigned)(p.nchunks * p.ngroups * nhb), (unsigned)p.batch);
+    hipLaunchKernelGGL(kern, grid, dim3(kScanThreads), lds, s, p, hpw);
+    return hipGetLastError();
+}
+
+// heads per workgroup: amortise phase A over up to 8 heads while keeping at
+// least ~512 workgroups in flight.
+static int scan_hpw(const Params& p) {
+    const int64_t units = p.batch * p.nchunks * p.nheads;
+    int64_t hpw = units / 512;
+    if (hpw > 8) hpw = 8;
+    if (hpw > p.heads_per_group) hpw = p.heads_per_group;
+    if (hpw < 1) hpw = 1;
+    return (int)hpw;
 }
 
 template <typename T, int PT, int NT, typename ST>
 static hipError_t launch_sc(const Params& p, hipStream_t s) {
-    const int lds = scan_lds_bytes<T, PT, NT>((int)p.chunk);
-    if (lds > kScanMaxLds) return hipErrorInvalidValue;
-    auto kern = ssd_chunk_scan_kernel<T, PT, NT, ST>;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (e != hipSuccess) return e;
-    dim3 grid((unsigned)p.nchunks, (unsigned)p.nheads, (unsigned)p.batch);
-    hipLaunchKernelGGL(kern, grid, dim3(256), lds, s, p);
-    return hipGetLastError();
+    using Cfg = ScanCfg<T, PT, NT, ST>;
+    const int Q = (int)p.chunk;
+    const int hpw = scan_hpw(p);
+    if (Cfg::lds(Q, 2, 2) <= kScanMaxLds) return launch_sc2<T, PT, NT, ST, 2, 2>(p, hpw, Cfg::lds(Q, 2, 2), s);
+    if (Cfg::lds(Q, 2, 1) <= kScanMaxLds) return launch_sc2<T, PT, NT, ST, 2, 1>(p, hpw, Cfg::lds(Q, 2, 1), s);
+    if (Cfg::lds(Q, 1, 1) <= kScanMaxLds) return launch_sc2<T, PT, NT, ST, 1, 1>(p, hpw, Cfg::lds(Q, 1, 1), s);
+    return hipErrorInvalidValue;
 }
 
 template <typename T, typename ST>
@@ -229,11 +402,12 @@ hipError_t launch_chunk_scan(const Params& p, int dtype, int state_dtype, hipStr
     return dispatch_sc<float, float>(p, s);
 }
 
-// LDS the chunk scan needs for (dtype, P, N, Q); used by argument checking.
-int chunk_scan_lds_bytes(int dtype, int64_t P, int64_t N, int64_t Q) {
-    const int pt = (int)((P + 31) / 32), nt = (int)((N + 31) / 32);
-    const int esz = dtype == 1 ? 2 : 4, pad = 16 / esz;
-    return pt * 32 * ((int)Q + pad) * esz + pt * 32 * (nt * 32 + pad) * esz + 2 * (int)Q * 4;
+// Smallest LDS the chunk scan needs for (dtype, state dtype, P, N, Q): single
+// x and h_c buffers; used by argument checking.
+int chunk_scan_lds_bytes(int dtype, int state_dtype, int64_t P, int64_t N, int64_t Q) {
+    const int esz = dtype == 1 ? 2 : 4, ssz = state_dtype == 1 ? 2 : 4;
+    const int pp = (int)((P + 31) / 32) * 32, np = (int)((N + 31) / 32) * 32;
+    return (int)Q * pp * esz + pp * np * ssz + 2 * 4 * (int)Q * 4;
 }
 
 }  // namespace ssd

@@ -9,114 +9,166 @@
 //
 //   S^T[p, n] = sum_j  x[j, p] * w_j * B[j, n],   w_j = exp(cs_last - cs_j) * dt_j
 //
-// a (P x Q) . (Q x N) product on the matrix cores. The product is stored
-// transposed ([P][N], n contiguous) because the chunk scan consumes the
-// carried state as a k-major (n-contiguous) operand.
+// a (P x Q) . (Q x N) product on the matrix cores, stored transposed ([P][N],
+// n contiguous) because the chunk scan consumes the carried state as a
+// k-major operand.
 //
-// Grid: (chunk, head, batch), 256 threads = 4 wavefronts. The chunk's tokens
-// are consumed in blocks of 64: x (scaled by w in fp32, then rounded to the
-// operand type) and B are staged transposed in LDS, and every wavefront
-// accumulates its share of the (P/32) x (N/32) output tiles.
+// Work split. One workgroup (4 wavefronts) takes one chunk and up to HPW heads
+// of one group, which share B. The chunk is consumed in blocks of 32 tokens,
+// double-buffered in LDS: while the matrix cores work on block k, the copy
+// engine path (global_load_lds, no registers) fills block k+1. B and x blocks
+// stay token-major in LDS (swizzled rows); the token-contiguous operand
+// fragments come out of LDS transpose reads, and w is applied to the x
+// fragment in registers. Each wavefront owns one head and PT/WPH of its
+// 32-row p tiles against all N/32 n tiles.
 #include "kernels.hpp"
-#include "transpose.hpp"
 
 namespace ssd {
 
-constexpr int kStateKB = 64;
-constexpr int kMaxChunk = 256;
+constexpr int kStateKB = 32;     // tokens per pipeline block
+
+template <typename T, int PT, int NT>
+struct StateCfg {
+    static constexpr int TILES = PT * NT;
+    static constexpr int WPH = TILES <= 8 ? 1 : TILES / 8;   // wavefronts per head
+    static constexpr int HPW = 4 / WPH;                      // heads per workgroup
+    static constexpr int PTW = PT / WPH;                     // p tiles per wavefront
+    static constexpr int EPC = 16 / (int)sizeof(T);          // elements per 16-byte chunk
+    static constexpr int XRC = PT * 32 / EPC;                // chunks per x row
+    static constexpr int BRC = NT * 32 / EPC;                // chunks per B row
+    static constexpr int XBYTES = kStateKB * XRC * 16;       // one head's x block
+    static constexpr int BBYTES = kStateKB * BRC * 16;
+    static constexpr int BUF = BBYTES + HPW * XBYTES;        // one pipeline buffer
+    static constexpr int LDS = 2 * BUF + HPW * 256 * 4;      // + w vectors (Q <= 256)
+};
 
 template <typename T, int PT, int NT, typename ST>
 __global__ __launch_bounds__(256) void ssd_chunk_state_kernel(Params p) {
-    constexpr int PP = PT * 32, NP = NT * 32;
-    constexpr int LD = kStateKB + 16 / (int)sizeof(T);     // 16-byte row padding
-    constexpr int TILES = PT * NT, TPW = (TILES + 3) / 4;
-    constexpr int XSB = (kStateKB / 8) * (PP / 8);          // 8x8 blocks of x per token block
-    constexpr int NSB = XSB + (kStateKB / 8) * (NP / 8);
-    __shared__ __attribute__((aligned(16))) T xs[PP * LD];
-    __shared__ __attribute__((aligned(16))) T bs[NP * LD];
-    __shared__ float wts[kMaxChunk];
+    using Cfg = StateCfg<T, PT, NT>;
+    constexpr int HPW = Cfg::HPW, WPH = Cfg::WPH, PTW = Cfg::PTW, NP = NT * 32;
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[Cfg::LDS];
+    float* wv = reinterpret_cast<float*>(smem + 2 * Cfg::BUF);   // [HPW][Q]
 
-    const int c = blockIdx.x;
-    const int64_t h = blockIdx.y, b = blockIdx.z;
     const int Q = (int)p.chunk;
-    const int64_t TL = p.seqlen, H = p.nheads, P = p.headdim, N = p.dstate, G = p.ngroups;
-    const int64_t g = h / p.heads_per_group;
+    const int64_t T_ = p.seqlen, H = p.nheads, P = p.headdim, N = p.dstate, G = p.ngroups;
+    const int64_t hpg = p.heads_per_group, nc = p.nchunks;
+    const int nhb = (int)((hpg + HPW - 1) / HPW);
+    int bx = blockIdx.x;
+    const int hb = bx % nhb;
+    bx /= nhb;
+    const int64_t g = bx % G;
+    const int c = (int)(bx / G);
+    const int64_t b = blockIdx.y;
+    const int64_t h0 = g * hpg + (int64_t)hb * HPW;
+    const int nh = (int)min<int64_t>(HPW, hpg - (int64_t)hb * HPW);
     const int64_t t0 = (int64_t)c * Q;
-    const float* csrow = p.cs + ((b * H + h) * p.nchunks + c) * Q;
-    const float last = csrow[Q - 1];
-    for (int j = threadIdx.x; j < Q; j += blockDim.x) {
-        const int64_t t = t0 + j;
-        wts[j] = (t < TL) ? exp2f((last - csrow[j]) * kLog2e) * p.dt[(b * TL + t) * H + h] : 0.0f;
-    }
+    const int qc = (int)min<int64_t>(Q, T_ - t0);
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wavefront
     const int hf = lane >> 5, l32 = lane & 31;
-    f32x16 acc[TPW];
-#pragma unroll
-    for (int k = 0; k < TPW; ++k) acc[k] = zero16();
+    const int64_t tok0 = b * T_ + t0;
+    constexpr int ESZ = (int)sizeof(T);
 
-    const T* xg = static_cast<const T*>(p.x);
-    const T* bg = static_cast<const T*>(p.B);
-    for (int kb = 0; kb < Q; kb += kStateKB) {
-        __syncthreads();  // wts ready (first block) / previous block consumed
-        for (int sb = threadIdx.x; sb < NSB; sb += blockDim.x) {
-            const bool isx = sb < XSB;
-            const int s2 = isx ? sb : sb - XSB;
-            const int ngrp = isx ? PP / 8 : NP / 8;
-            const int col = (s2 % ngrp) * 8, tg = s2 / ngrp;
-            const int64_t limit = isx ? P : N;
-            float v[8][8];
-#pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                const int j = kb + tg * 8 + r;
-                const int64_t t = t0 + j;
-                const bool ok = (j < Q) && (t < TL) && (col < limit);
-                const T* src = isx ? xg + ((b * TL + t) * H + h) * P + col
-                                   : bg + ((b * TL + t) * G + g) * N + col;
-                load_row8<T>(v[r], src, ok);
-                if (isx) {
-                    const float s = ok ? wts[j] : 0.0f;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) v[r][e] *= s;
-                }
-            }
-            store_transposed8<T>((isx ? xs : bs) + col * LD + tg * 8, LD, v);
+    // decay-to-chunk-end weights w_j for every head of the block
+    const float* csbase = p.cs + ((b * H + h0) * nc + c) * Q;
+    const float* dtbase = p.dt + tok0 * H + h0;
+    for (int idx = threadIdx.x; idx < HPW * Q; idx += blockDim.x) {
+        const int hq = idx / Q, j = idx % Q;
+        float wj = 0.0f;
+        if (hq < nh && j < qc) {
+            const float* csr = csbase + (int64_t)hq * nc * Q;
+            wj = exp2f((ldg(csr + Q - 1) - ldg(csr + j)) * kLog2e) * ldg(dtbase + hq + (uint32_t)j * (uint32_t)H);
         }
+        wv[hq * Q + j] = wj;
+    }
+
+    const unsigned char* bbase = static_cast<const unsigned char*>(p.B) + (tok0 * G + g) * N * ESZ;
+    const unsigned char* xbase = static_cast<const unsigned char*>(p.x) + (tok0 * H + h0) * P * ESZ;
+    const uint32_t bstride = (uint32_t)(G * N * ESZ), xstride = (uint32_t)(H * P * ESZ);
+    const int xvalid = (int)(P * ESZ / 16), bvalid = (int)(N * ESZ / 16);
+    auto issue = [&](int blk, int buf) {
+        unsigned char* base = smem + buf * Cfg::BUF;
+        // rows of the block past the chunk's last token re-read that token (their
+        // weight w is 0); a block wholly past it reads only that token
+        const int r0 = min(blk * kStateKB, qc - 1);
+        const int vrows = min(kStateKB, qc - r0);
+        dma_tile<Cfg::BRC>(base, kStateKB, vrows, bvalid, bbase + (uint32_t)r0 * bstride, bstride, wave, 4, lane);
+        for (int hq = 0; hq < nh; ++hq)
+            dma_tile<Cfg::XRC>(base + Cfg::BBYTES + hq * Cfg::XBYTES, kStateKB, vrows, xvalid,
+                               xbase + (uint32_t)r0 * xstride + (int64_t)hq * P * ESZ, xstride, wave, 4, lane);
+    };
+
+    const int hh = wave / WPH;           // this wavefront's head within the block
+    const int pt0 = (wave % WPH) * PTW;  // its first p tile
+    const bool active = hh < nh;
+    f32x16 acc[PTW][NT];
+#pragma unroll
+    for (int i = 0; i < PTW; ++i)
+#pragma unroll
+        for (int n = 0; n < NT; ++n) acc[i][n] = zero16();
+
+    const int nblk = Q / kStateKB;
+    issue(0, 0);
+    wait_vmem();
+    __syncthreads();
+    for (int blk = 0; blk < nblk; ++blk) {
+        const int buf = blk & 1;
+        if (blk + 1 < nblk) issue(blk + 1, buf ^ 1);
+        if (active) {
+            const unsigned char* base = smem + buf * Cfg::BUF;
+            const T* btile = reinterpret_cast<const T*>(base);
+            const T* xtile = reinterpret_cast<const T*>(base + Cfg::BBYTES + hh * Cfg::XBYTES);
+            const float* wrow = wv + hh * Q + blk * kStateKB;
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                auto rowk = [s](int hf_, int e) { return 16 * s + 8 * hf_ + e; };
+                const f32x4 w0 = *reinterpret_cast<const f32x4*>(wrow + 16 * s + 8 * hf);
+                const f32x4 w1 = *reinterpret_cast<const f32x4*>(wrow + 16 * s + 8 * hf + 4);
+                typename Vec8<T>::type xf[PTW], bf[NT];
+#pragma unroll
+                for (int i = 0; i < PTW; ++i) {
+                    const auto raw = frag_tr<Cfg::XRC>(xtile, (pt0 + i) * 32, rowk, lane);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        xf[i][e] = from_f32<T>(to_f32(raw[e]) * (e < 4 ? w0[e] : w1[e - 4]));
+                }
+#pragma unroll
+                for (int n = 0; n < NT; ++n) bf[n] = frag_tr<Cfg::BRC>(btile, n * 32, rowk, lane);
+#pragma unroll
+                for (int i = 0; i < PTW; ++i)
+#pragma unroll
+                    for (int n = 0; n < NT; ++n) mma_k16(acc[i][n], xf[i], bf[n]);
+            }
+        }
+        wait_vmem();
         __syncthreads();
+    }
+
+    if (active) {
+        const int64_t h = h0 + hh;
+        ST* sg = static_cast<ST*>(p.states) + ((b * nc + c) * H + h) * P * N;   // [P][N] of this head
 #pragma unroll
-        for (int ks = 0; ks < kStateKB / 16; ++ks) {
+        for (int i = 0; i < PTW; ++i) {
 #pragma unroll
-            for (int k = 0; k < TPW; ++k) {
-                const int tile = wave + 4 * k;
-                if (tile < TILES) {
-                    const int pt = tile / NT, nt = tile % NT;
-                    const auto a = load8(xs + (pt * 32 + l32) * LD + ks * 16 + hf * 8);
-                    const auto bb = load8(bs + (nt * 32 + l32) * LD + ks * 16 + hf * 8);
-                    mma_k16(acc[k], a, bb);
+            for (int n = 0; n < NT; ++n) {
+                const int64_t col = n * 32 + l32;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int64_t pr = (pt0 + i) * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+                    if (pr < P && col < N) stg<ST>(sg + (uint32_t)(pr * N + col), from_f32<ST>(acc[i][n][r]));
                 }
             }
         }
     }
-
-    ST* sg = static_cast<ST*>(p.states) + ((b * p.nchunks + c) * H + h) * P * N;
-#pragma unroll
-    for (int k = 0; k < TPW; ++k) {
-        const int tile = wave + 4 * k;
-        if (tile < TILES) {
-            const int pt = tile / NT, nt = tile % NT;
-            const int64_t n = nt * 32 + l32;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int64_t pr = pt * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-                if (pr < P && n < N) sg[pr * N + n] = from_f32<ST>(acc[k][r]);
-            }
-        }
-    }
+    (void)NP;
 }
 
 template <typename T, int PT, int NT, typename ST>
 static hipError_t launch_cs(const Params& p, hipStream_t s) {
-    dim3 grid((unsigned)p.nchunks, (unsigned)p.nheads, (unsigned)p.batch);
+    using Cfg = StateCfg<T, PT, NT>;
+    const int64_t nhb = (p.heads_per_group + Cfg::HPW - 1) / Cfg::HPW;
+    dim3 grid((unsigned)(p.nchunks * p.ngroups * nhb), (unsigned)p.batch);
     hipLaunchKernelGGL((ssd_chunk_state_kernel<T, PT, NT, ST>), grid, dim3(256), 0, s, p);
     return hipGetLastError();
 }

@@ -6,7 +6,7 @@
 #include "kernels.hpp"
 
 namespace ssd {
-int chunk_scan_lds_bytes(int dtype, int64_t P, int64_t N, int64_t Q);
+int chunk_scan_lds_bytes(int dtype, int state_dtype, int64_t P, int64_t N, int64_t Q);
 }
 
 namespace {
@@ -67,7 +67,7 @@ const char* ssd_status_string(ssd_status s) {
         case SSD_ERR_UNSUPPORTED:
             return "unsupported configuration: headdim in {16,32,64,128}, dstate in {16,32,64,128,256}, "
                    "chunk_size in {32,64,128,256}, dtype fp32/bf16, bf16 states only with bf16 inputs, "
-                   "and (fp32) the chunk tile must fit in LDS";
+                   "and the chunk scan's x and state tiles must fit in LDS (Q*P*esize + P*N*ssize <= ~156 KB)";
         case SSD_ERR_MISALIGNED: return "a tensor pointer is not 16-byte aligned";
         case SSD_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than ssd_workspace_size()";
         case SSD_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
@@ -89,7 +89,7 @@ ssd_status ssd_check_dims(const ssd_dims* d) {
     if (d->dtype != SSD_F32 && d->dtype != SSD_BF16) return SSD_ERR_UNSUPPORTED;
     if (d->state_dtype != SSD_F32 && d->state_dtype != SSD_BF16) return SSD_ERR_UNSUPPORTED;
     if (d->state_dtype == SSD_BF16 && d->dtype != SSD_BF16) return SSD_ERR_UNSUPPORTED;
-    if (ssd::chunk_scan_lds_bytes(d->dtype, d->headdim, d->dstate, d->chunk_size) > kMaxLds)
+    if (ssd::chunk_scan_lds_bytes(d->dtype, d->state_dtype, d->headdim, d->dstate, d->chunk_size) > kMaxLds)
         return SSD_ERR_UNSUPPORTED;
     // grid limits: nchunks and nheads go in grid.x / grid.y, batch in grid.z
     if (nchunks_of(d) > INT32_MAX || d->nheads > 65535 || d->batch > 65535) return SSD_ERR_UNSUPPORTED;

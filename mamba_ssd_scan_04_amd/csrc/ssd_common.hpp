@@ -120,3 +120,140 @@ __device__ __forceinline__ int frag_token(int q) {
 }
 
 }  // namespace ssd
+
+// ---- LDS tiles ---------------------------------------------------------------
+//
+// Row-major tiles in LDS are addressed in 16-byte chunks with an XOR swizzle
+// of the chunk index by the row, so that the two access patterns the kernels
+// use are (nearly) free of bank conflicts:
+//  (a) transpose reads: 4 consecutive rows x 64 contiguous bytes per half wave;
+//  (b) row reads: 32 consecutive rows, the same 16-byte chunk of each.
+// RC is the number of 16-byte chunks per row (a power of two >= 4).
+namespace ssd {
+
+template <int RC>
+__device__ __forceinline__ int swz(int r) {
+    if constexpr (RC >= 16) return ((r & 3) << 2) | ((r >> 2) & 3);
+    else if constexpr (RC == 8) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+    else return (r >> 2) & 3;
+}
+
+// byte offset of (row r, byte b within the row) in a swizzled tile
+template <int RC>
+__device__ __forceinline__ int tile_byte(int r, int b) {
+    return r * RC * 16 + (((b >> 4) ^ swz<RC>(r)) << 4) + (b & 15);
+}
+
+// Asynchronous global -> LDS copy of a rows x RC-chunk tile. Every lane of a
+// wavefront copies one 16-byte chunk per instruction straight into LDS (no
+// registers); instruction k of the tile writes LDS bytes [1024 k, 1024 k + 1024).
+// The source of physical chunk (r, pc) is logical chunk c = pc ^ swz(r) of
+// row r: gbase + r * row_stride + 16 c, with r clamped to valid_rows - 1 and c
+// to valid_chunks - 1 (rows or columns past the data are filled with copies of
+// real data: the kernels only ever give them zero weight or leave their
+// outputs unstored). gbase is uniform; offsets are 32-bit.
+template <int RC>
+__device__ __forceinline__ void dma_tile(unsigned char* lds, int rows, int valid_rows, int valid_chunks,
+                                         const unsigned char* gbase, uint32_t row_stride, int wave,
+                                         int nwaves, int lane) {
+    const int total = rows * RC;   // a multiple of 64
+    for (int k = wave; k * 64 < total; k += nwaves) {
+        const int P = k * 64 + lane;
+        const int r = P / RC;
+        int c = (P % RC) ^ swz<RC>(r);
+        c = c < valid_chunks ? c : valid_chunks - 1;
+        const int rr = r < valid_rows ? r : valid_rows - 1;
+        const unsigned char* src = gbase + ((uint32_t)rr * row_stride + 16u * (uint32_t)c);
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                         (__attribute__((address_space(3))) void*)(lds + k * 1024), 16, 0, 0);
+    }
+}
+
+// Loads through explicit global-address-space pointers (not flat).
+__device__ __forceinline__ bf16x8 ldg8(const bf16* p) {
+    return *(const __attribute__((address_space(1))) bf16x8*)p;
+}
+__device__ __forceinline__ f32x8 ldg8(const float* p) {
+    const f32x4 lo = *(const __attribute__((address_space(1))) f32x4*)p;
+    const f32x4 hi = *(const __attribute__((address_space(1))) f32x4*)(p + 4);
+    f32x8 v;
+    v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
+    v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
+    return v;
+}
+__device__ __forceinline__ float ldg(const float* p) { return *(const __attribute__((address_space(1))) float*)p; }
+template <typename T> __device__ __forceinline__ void stg(T* p, T v) { *(__attribute__((address_space(1))) T*)p = v; }
+
+// Wait until this wavefront's outstanding vector memory operations (including
+// the LDS copies above) have completed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+
+// 8 k-elements of a matrix-core operand from a row-major swizzled LDS tile
+// whose rows are the k index: lane (l32, hf) receives rows rowk(hf, e),
+// e = 0..7, of column col0 + l32. bf16 uses two ds_read_b64_tr_b16: within a
+// group of 16 lanes, result lane i slot s is element i%4 of the 8 bytes at the
+// address of lane 4s + i/4, so lane 16q + 4s + j points at row rowk(hf, s)
+// (s + 4 for the second read), columns col0 + 16(q%2) + 4j .. +3.
+template <int RC, typename RowK>
+__device__ __forceinline__ bf16x8 frag_tr(const bf16* tile, int col0, RowK rowk, int lane) {
+    const int q = lane >> 4, s = (lane >> 2) & 3, j = lane & 3, hf = lane >> 5;
+    const int cb = (col0 + 16 * (q & 1) + 4 * j) * 2;   // byte within the row
+    const unsigned char* base = reinterpret_cast<const unsigned char*>(tile);
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    lds_s16x4* pa = (lds_s16x4*)(base + tile_byte<RC>(rowk(hf, s), cb));
+    lds_s16x4* pb = (lds_s16x4*)(base + tile_byte<RC>(rowk(hf, s + 4), cb));
+    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(pa);
+    const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(pb);
+    // whole-vector bit casts (casting single ext-vector elements miscompiles)
+    const bf16x4 av = __builtin_bit_cast(bf16x4, a);
+    const bf16x4 bv = __builtin_bit_cast(bf16x4, b);
+    return __builtin_shufflevector(av, bv, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+template <int RC, typename RowK>
+__device__ __forceinline__ f32x8 frag_tr(const float* tile, int col0, RowK rowk, int lane) {
+    const int hf = lane >> 5, l32 = lane & 31;
+    const unsigned char* base = reinterpret_cast<const unsigned char*>(tile);
+    f32x8 out;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        out[e] = *reinterpret_cast<const float*>(base + tile_byte<RC>(rowk(hf, e), (col0 + l32) * 4));
+    return out;
+}
+
+// 8 consecutive elements (one or two 16-byte chunks) of row r starting at
+// element col (a multiple of 8) from a swizzled LDS tile.
+template <int RC>
+__device__ __forceinline__ bf16x8 row8(const bf16* tile, int r, int col) {
+    return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const unsigned char*>(tile) +
+                                            tile_byte<RC>(r, col * 2));
+}
+template <int RC>
+__device__ __forceinline__ f32x8 row8(const float* tile, int r, int col) {
+    const unsigned char* base = reinterpret_cast<const unsigned char*>(tile);
+    const f32x4 lo = *reinterpret_cast<const f32x4*>(base + tile_byte<RC>(r, col * 4));
+    const f32x4 hi = *reinterpret_cast<const f32x4*>(base + tile_byte<RC>(r, col * 4 + 16));
+    f32x8 v;
+    v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
+    v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
+    return v;
+}
+
+template <typename T> __device__ __forceinline__ typename Vec8<T>::type cvt8(const bf16x8& v) {
+    if constexpr (sizeof(T) == 2) return v;
+    else {
+        f32x8 o;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = to_f32(v[e]);
+        return o;
+    }
+}
+template <typename T> __device__ __forceinline__ typename Vec8<T>::type cvt8(const f32x8& v) {
+    typename Vec8<T>::type o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = from_f32<T>(v[e]);
+    return o;
+}
+
+}  // namespace ssd

@@ -72,7 +72,9 @@ def dims(**kw):
     (dict(dtype="bf16", state_dtype="bf16"), OK),
     (dict(dtype="fp32", headdim=16, dstate=16, chunk_size=64), OK),
     (dict(dtype="fp32", headdim=128, dstate=256, chunk_size=256), UNSUP),  # fp32 tile > LDS
-    (dict(headdim=128, dstate=256, chunk_size=256), OK),
+    (dict(headdim=128, dstate=256, chunk_size=256), UNSUP),  # x + fp32 state tiles > LDS
+    (dict(headdim=128, dstate=256, chunk_size=256, state_dtype="bf16"), OK),
+    (dict(headdim=128, dstate=256, chunk_size=64), OK),
 ])
 def test_check_dims(lib, kw, code):
     assert ssd.ssd_check_dims(dims(**kw)) == code
@@ -96,7 +98,9 @@ def test_workspace_size(lib):
     # monotonic in every size
     w = ssd.ssd_workspace_size(d)
     for k, v in dict(batch=3, seqlen=513, nheads=10, headdim=128, dstate=256).items():
-        assert ssd.ssd_workspace_size(dims(**k and {k: v})) > w
+        bigger = dims(**{k: v, "state_dtype": "bf16"}) if k in ("headdim", "dstate") else dims(**{k: v})
+        base = ssd.ssd_workspace_size(dims(state_dtype="bf16")) if k in ("headdim", "dstate") else w
+        assert ssd.ssd_workspace_size(bigger) > base
     # ragged T rounds up to whole chunks
     assert ssd.ssd_workspace_size(dims(seqlen=300)) == ssd.ssd_workspace_size(dims(seqlen=512))
 

@@ -55,10 +55,11 @@ def test_chunk_sizes(Q):
     check(w, inputs.generate_slow_decay(w, seed=3))
 
 
-@pytest.mark.parametrize("P,N", [(16, 16), (32, 64), (64, 16), (64, 256), (128, 128), (128, 256), (16, 256)])
-def test_head_and_state_dims(P, N):
+@pytest.mark.parametrize("P,N,state", [(16, 16, "fp32"), (32, 64, "fp32"), (64, 16, "fp32"), (64, 256, "fp32"),
+                                         (128, 128, "fp32"), (128, 256, "bf16"), (16, 256, "fp32")])
+def test_head_and_state_dims(P, N, state):
     w = workload("m125", batch=1, seqlen=520, nheads=3, headdim=P, dstate=N)
-    check(w, inputs.generate_slow_decay(w, seed=4))
+    check(w, inputs.generate_slow_decay(w, seed=4), state)
 
 
 @pytest.mark.parametrize("H,G", [(6, 2), (6, 6), (24, 8)])
