@@ -123,6 +123,22 @@ def cpu_baseline(inp, w, budget_s: float = 10.0) -> dict:
                       f"fp64 recurrence in {secs:.2f} s on {threads} threads; tokens/s = sequences*T/H/s"}
 
 
+def calibrate_copy(torch) -> int:
+    """A plain device-to-device copy of a known size: under rocprofv3 --pmc
+    FETCH_SIZE / WRITE_SIZE its counters give the scale from counter units to
+    bytes (reads and writes of exactly `nbytes` per dispatch)."""
+    nbytes = 1 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_read_per_dispatch": nbytes,
+                      "bytes_written_per_dispatch": nbytes}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -132,6 +148,8 @@ def main() -> int:
     ap.add_argument("--state-dtype", default="fp32", choices=["fp32", "bf16"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy 5 times (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -147,6 +165,8 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
+    if args.calibrate_copy:
+        return calibrate_copy(torch)
     w = inputs.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     inp = inputs.generate(w, seed=0)
