@@ -30,7 +30,8 @@
 namespace ssd {
 
 constexpr int kScanMaxLds = 160 * 1024;
-constexpr int kScanThreads = 256;
+constexpr int kScanThreads = 512;
+constexpr int kScanWaves = kScanThreads / 64;
 
 template <typename T, int PT, int NT, typename ST>
 struct ScanCfg {
@@ -39,179 +40,43 @@ struct ScanCfg {
     static constexpr int HRC = NT * 32 * (int)sizeof(ST) / 16; // chunks per h_c row
     static constexpr int HBYTES = PT * 32 * HRC * 16;          // one head's h_c tile
     static constexpr int KS = NT * 2;                          // k16 steps over n
+    static constexpr int YBYTES = 8 * PT * 32 * (int)sizeof(T);    // per-wave y staging: 8 rows
+    static constexpr int YCHUNKS = YBYTES / 16;                 // 16-byte row segments staged
+    static constexpr int NSTORE = (YCHUNKS + 63) / 64;          // store instructions per 8 rows
     __host__ __device__ static int xbytes(int Q) { return Q * XRC * 16; }
     __host__ __device__ static int vbytes(int Q) { return 4 * Q * 4; }
     // bytes of LDS with nbx x buffers and nbh h_c buffers
-    __host__ __device__ static int lds(int Q, int nbx, int nbh) { return nbx * xbytes(Q) + nbh * HBYTES + 2 * vbytes(Q); }
+    __host__ __device__ static int lds(int Q, int nbx, int nbh) {
+        return nbx * xbytes(Q) + nbh * HBYTES + 2 * vbytes(Q) + kScanWaves * YBYTES;
+    }
 };
 
-// Per-head LDS views used by one row tile's math.
-template <typename T, typename ST>
-struct HeadView {
-    const T* xt;      // x tile, token-major, swizzled
-    const ST* ht;     // h_c^T tile [P][N], swizzled
-    const float* c2;  // cs * log2(e)
-    const float* dt;  // dt (0 past the end)
-    const float* ecs; // exp(cs)
-    const float* u;   // exp(cs_r - cs_i) dt_i, r = the 32-token tile's last token
-};
-
-// C B^T row of tiles for row tile rt: key tiles kt < rt into cb[kt], the
-// diagonal tile kt == rt into cbd; rows past qc and columns past N are zero.
-// B fragments for key tile kt+1 are loaded while tile kt is multiplied.
-template <typename T, int KS, int SLOTS>
-__device__ __forceinline__ void cb_row(typename Vec8<T>::type (&cb)[SLOTS][2], typename Vec8<T>::type (&cbd)[2],
-                                       const typename Vec8<T>::type (&creg)[KS], const T* bbase, uint32_t bcs,
-                                       int rt, int qc, int N, int l32, int hf) {
-    using V8 = typename Vec8<T>::type;
-    const int nlast = N - 8;
-    auto off = [&](int row, int ks) {
-        return (uint32_t)min(row, qc - 1) * bcs + (uint32_t)min(ks * 16 + hf * 8, nlast);
-    };
-    V8 bnext[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) bnext[ks] = ldg8(bbase + off(l32, ks));
-#pragma unroll
-    for (int kt = 0; kt <= SLOTS; ++kt) {
-        if (kt <= rt) {
-            V8 bcur[KS];
-            const bool rok = kt * 32 + l32 < qc;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) bcur[ks] = (rok && ks * 16 + hf * 8 < N) ? bnext[ks] : zero8<T>();
-            if (kt < rt) {
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) bnext[ks] = ldg8(bbase + off((kt + 1) * 32 + l32, ks));
-            }
-            f32x16 acc = zero16();
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) mma_k16(acc, bcur[ks], creg[ks]);
-            V8 lo, hi;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                lo[e] = from_f32<T>(acc[e]);
-                hi[e] = from_f32<T>(acc[8 + e]);
-            }
-            if (kt < rt) {
-                cb[kt < SLOTS ? kt : SLOTS - 1][0] = lo;
-                cb[kt < SLOTS ? kt : SLOTS - 1][1] = hi;
-            } else {
-                cbd[0] = lo;
-                cbd[1] = hi;
-            }
-        }
-    }
-}
-
-// One head's output for row tile rt: (C . h_c) scaled by exp(cs_j), plus the
-// decayed, masked C B^T tiles times x, plus D x; stores y. rt, qc and P arrive
-// through an empty asm so per-element compares stay inside the head loop
-// instead of being hoisted (as lane masks) across it.
-template <typename T, int PT, int KS, int XRC, int HRC, int SLOTS, typename ST>
-__device__ __forceinline__ void row_tile_head(const typename Vec8<T>::type (&cb)[SLOTS][2],
-                                              const typename Vec8<T>::type (&cbd)[2],
-                                              const typename Vec8<T>::type (&creg)[KS], const HeadView<T, ST>& v,
-                                              int rt, bool carried, float Dh, T* yh, uint32_t ystride, int qc,
-                                              int P, int lane) {
-    using V8 = typename Vec8<T>::type;
-    const int hf = lane >> 5, l32 = lane & 31;
-    int jl = rt * 32 + l32;
-    asm volatile("" : "+v"(jl), "+v"(qc), "+v"(P));
-    f32x16 acc[PT];
-#pragma unroll
-    for (int pt = 0; pt < PT; ++pt) acc[pt] = zero16();
-    if (carried) {
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-            for (int pt = 0; pt < PT; ++pt)
-                mma_k16(acc[pt], creg[ks], cvt8<T>(row8<HRC>(v.ht, pt * 32 + l32, ks * 16 + hf * 8)));
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-            const f32x4 e4 = *reinterpret_cast<const f32x4*>(v.ecs + rt * 32 + 8 * gq + 4 * hf);
-#pragma unroll
-            for (int pt = 0; pt < PT; ++pt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) acc[pt][4 * gq + r] *= e4[r];
-        }
-    }
-    const float c2j = v.c2[jl];
-    // key tiles off the diagonal: M = CB * exp(cs_j - cs_r) * u_i, no mask
-#pragma unroll
-    for (int kt = 0; kt < SLOTS; ++kt) {
-        if (kt < rt) {
-            const float vj = exp2f(c2j - v.c2[kt * 32 + 31]);
-            V8 aop[2];
-#pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                const f32x4 u4 = *reinterpret_cast<const f32x4*>(v.u + kt * 32 + 8 * gq + 4 * hf);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int idx = 4 * gq + r;
-                    aop[idx >> 3][idx & 7] = from_f32<T>(to_f32(cb[kt][idx >> 3][idx & 7]) * vj * u4[r]);
-                }
-            }
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                auto rowk = [kt, s](int hf_, int e) { return kt * 32 + 16 * s + 8 * (e >> 2) + 4 * hf_ + (e & 3); };
-#pragma unroll
-                for (int pt = 0; pt < PT; ++pt) mma_k16(acc[pt], aop[s], frag_tr<XRC>(v.xt, pt * 32, rowk, lane));
-            }
-        }
-    }
-    // the diagonal tile: direct decay; the causal mask (i <= j) enters as a
-    // -inf exponent for i > j, so exp2 gives exactly 0 with no lane masks
-    {
-        V8 aop[2];
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-            const int ib = rt * 32 + 8 * gq + 4 * hf;
-            const f32x4 ci = *reinterpret_cast<const f32x4*>(v.c2 + ib);
-            const f32x4 di = *reinterpret_cast<const f32x4*>(v.dt + ib);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int idx = 4 * gq + r;
-                const float pen = __int_as_float(((jl - (ib + r)) >> 31) & (int)0xff800000u);
-                const float m = to_f32(cbd[idx >> 3][idx & 7]) * exp2f((c2j - ci[r]) + pen) * di[r];
-                aop[idx >> 3][idx & 7] = from_f32<T>(m);
-            }
-        }
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            auto rowk = [rt, s](int hf_, int e) { return rt * 32 + 16 * s + 8 * (e >> 2) + 4 * hf_ + (e & 3); };
-#pragma unroll
-            for (int pt = 0; pt < PT; ++pt) mma_k16(acc[pt], aop[s], frag_tr<XRC>(v.xt, pt * 32, rowk, lane));
-        }
-    }
-    // epilogue: + D x_j (the diagonal tile's x fragments have the accumulator's rows)
-#pragma unroll
-    for (int pt = 0; pt < PT; ++pt) {
-        const int pc = pt * 32 + l32;
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            auto rowk = [rt, s](int hf_, int e) { return rt * 32 + 16 * s + 8 * (e >> 2) + 4 * hf_ + (e & 3); };
-            const V8 xd = frag_tr<XRC>(v.xt, pt * 32, rowk, lane);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int r = 8 * s + e;
-                const int j = rt * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-                if (j < qc && pc < P)
-                    stg<T>(yh + (uint32_t)j * ystride + pc, from_f32<T>(acc[pt][r] + Dh * to_f32(xd[e])));
-            }
-        }
+// x fragment (B operand of Y += M . X, k = key token in fragment order) at
+// 16-row group g16 of column tile pt: bf16 through two transpose reads at
+// precomputed offsets; fp32 through plain reads.
+template <typename T, int XRC>
+__device__ __forceinline__ typename Vec8<T>::type x_frag(const unsigned char* xt, int g16, int pt, const int (&xoa)[4],
+                                                        const int (&xob)[4], int lane) {
+    if constexpr (sizeof(T) == 2) {
+        return frag_tr_at(xt + g16 * 16 * XRC * 16, xoa[pt], xob[pt]);
+    } else {
+        auto rowk = [g16](int hf_, int e) { return g16 * 16 + 8 * (e >> 2) + 4 * hf_ + (e & 3); };
+        return frag_tr<XRC>(reinterpret_cast<const float*>(xt), pt * 32, rowk, lane);
     }
 }
 
 template <typename T, int PT, int NT, typename ST, int NBX, int NBH>
-__global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void ssd_chunk_scan_kernel(Params p, int hpw) {
+__global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, int hpw) {
     using Cfg = ScanCfg<T, PT, NT, ST>;
     using V8 = typename Vec8<T>::type;
-    constexpr int KS = Cfg::KS;
+    constexpr int KS = Cfg::KS, XRC = Cfg::XRC, HRC = Cfg::HRC;
     constexpr int ESZ = (int)sizeof(T), SSZ = (int)sizeof(ST);
     extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
     const int Q = (int)p.chunk;
     const int XB = Cfg::xbytes(Q), VB = Cfg::vbytes(Q);
     unsigned char* const hb0 = smem + NBX * XB;
     float* const vb0 = reinterpret_cast<float*>(hb0 + NBH * Cfg::HBYTES);
+    unsigned char* const yst0 = reinterpret_cast<unsigned char*>(vb0) + 2 * VB;
 
     // ---- block coordinates (uniform) ----
     const int64_t T_ = p.seqlen, H = p.nheads, P = p.headdim, N = p.dstate, G = p.ngroups;
@@ -232,11 +97,12 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(1,
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int hf = lane >> 5, l32 = lane & 31;
-    // row tiles of this wavefront: with 8 tiles, w and 7 - w (causal work
-    // (rt + 1) + (8 - rt) = 9 key tiles each); with fewer, tile w alone
+    // Row tile of this wavefront. Waves w and w+4 share a SIMD; with 8 tiles
+    // they take tiles s and 7 - s, so every SIMD carries 9 key tiles of work.
     const int RT = Q / 32;
-    const int rs = wave < RT ? wave : -1;                 // short row (<= 3 when RT == 8)
-    const int rl = RT == 8 ? 7 - wave : -1;               // long row (>= 4)
+    const int rt = RT == 8 ? (wave < 4 ? wave : 11 - wave) : (wave < RT ? wave : -1);
+    const bool active = rt >= 0;
+    unsigned char* const yst = yst0 + wave * Cfg::YBYTES;
 
     const uint32_t bcs = (uint32_t)(G * N);
     const T* cbase = static_cast<const T*>(p.C) + (tok0 * G + g) * N;
@@ -244,19 +110,17 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(1,
     const unsigned char* xbase = static_cast<const unsigned char*>(p.x) + (tok0 * H + h0) * P * ESZ;
     const uint32_t xstride = (uint32_t)(H * P * ESZ);
     const unsigned char* sbase = static_cast<const unsigned char*>(p.states) + ((b * nc + c) * H + h0) * P * N * SSZ;
-    T* ybase = static_cast<T*>(p.y) + (tok0 * H + h0) * P;
-    const uint32_t ystride = (uint32_t)(H * P);
+    unsigned char* ybase = static_cast<unsigned char*>(p.y) + (tok0 * H + h0) * P * ESZ;
     const float* csbase = p.cs + ((b * H + h0) * nc + c) * Q;
     const float* dtbase = p.dt + tok0 * H + h0;
     const int xvalid = (int)(P * ESZ / 16), hvalid = (int)(N * SSZ / 16);
 
     auto issue_x = [&](int hh, int buf) {
-        dma_tile<Cfg::XRC>(smem + buf * XB, Q, qc, xvalid, xbase + (int64_t)hh * P * ESZ, xstride, wave,
-                           kScanThreads / 64, lane);
+        dma_tile<XRC>(smem + buf * XB, Q, qc, xvalid, xbase + (int64_t)hh * P * ESZ, xstride, wave, kScanWaves, lane);
     };
     auto issue_h = [&](int hh, int buf) {
-        dma_tile<Cfg::HRC>(hb0 + buf * Cfg::HBYTES, PT * 32, (int)P, hvalid, sbase + (int64_t)hh * P * N * SSZ,
-                           (uint32_t)(N * SSZ), wave, kScanThreads / 64, lane);
+        dma_tile<HRC>(hb0 + buf * Cfg::HBYTES, PT * 32, (int)P, hvalid, sbase + (int64_t)hh * P * N * SSZ,
+                      (uint32_t)(N * SSZ), wave, kScanWaves, lane);
     };
     float vcs = 0.0f, vcr = 0.0f, vdt = 0.0f;   // thread i holds token i of the next head
     auto load_vec = [&](int hh) {
@@ -287,27 +151,66 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(1,
         load_vec(0);
     }
 
-    // ---- phase A: C rows and C B^T rows of tiles, once per workgroup ----
+    // ---- phase A: this wave's C rows and C B^T row of tiles, once per workgroup ----
     const int nlast = (int)N - 8;
-    V8 cs_reg[KS], cl_reg[KS];        // C rows of the short / long row tile
-    V8 cb_s[3][2], cb_l[7][2];        // their C B^T tiles off the diagonal (kt < rt)
-    V8 cbd_s[2], cbd_l[2];            // and on it
-    auto load_c = [&](V8 (&cr)[KS], int rt) {
-        const int j = rt * 32 + l32;
+    V8 creg[KS];
+    V8 cb[7][2];     // key tiles kt < rt
+    V8 cbd[2];       // the diagonal tile
+    if (active) {
+        auto off = [&](int row, int ks) {
+            return (uint32_t)min(row, qc - 1) * bcs + (uint32_t)min(ks * 16 + hf * 8, nlast);
+        };
+        const int jl = rt * 32 + l32;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const V8 raw = ldg8(cbase + (uint32_t)min(j, qc - 1) * bcs + (uint32_t)min(ks * 16 + hf * 8, nlast));
-            cr[ks] = (j < qc && ks * 16 + hf * 8 < (int)N) ? raw : zero8<T>();
+            const V8 raw = ldg8(cbase + off(jl, ks));
+            creg[ks] = (jl < qc && ks * 16 + hf * 8 < (int)N) ? raw : zero8<T>();
         }
-    };
-    if (rs >= 0) {
-        load_c(cs_reg, rs);
-        cb_row<T, KS, 3>(cb_s, cbd_s, cs_reg, bbase, bcs, rs, qc, (int)N, l32, hf);
+        V8 bnext[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) bnext[ks] = ldg8(bbase + off(l32, ks));
+#pragma unroll
+        for (int kt = 0; kt < 8; ++kt) {
+            if (kt <= rt) {
+                V8 bcur[KS];
+                const bool rok = kt * 32 + l32 < qc;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) bcur[ks] = (rok && ks * 16 + hf * 8 < (int)N) ? bnext[ks] : zero8<T>();
+                if (kt < rt) {
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) bnext[ks] = ldg8(bbase + off((kt + 1) * 32 + l32, ks));
+                }
+                f32x16 acc = zero16();
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) mma_k16(acc, bcur[ks], creg[ks]);
+                V8 lo, hi;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    lo[e] = from_f32<T>(acc[e]);
+                    hi[e] = from_f32<T>(acc[8 + e]);
+                }
+                if (kt < rt) {
+                    cb[kt < 7 ? kt : 6][0] = lo;
+                    cb[kt < 7 ? kt : 6][1] = hi;
+                } else {
+                    cbd[0] = lo;
+                    cbd[1] = hi;
+                }
+            }
+        }
     }
-    if (rl >= 0) {
-        load_c(cl_reg, rl);
-        cb_row<T, KS, 7>(cb_l, cbd_l, cl_reg, bbase, bcs, rl, qc, (int)N, l32, hf);
+
+    // lane offsets of the x fragments (fragment order), per column tile
+    int xoa[4] = {0, 0, 0, 0}, xob[4] = {0, 0, 0, 0};
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt)
+            frag_tr_offsets<XRC>(pt * 32, [](int hf_, int e) { return 8 * (e >> 2) + 4 * hf_ + (e & 3); }, lane,
+                                 xoa[pt], xob[pt]);
     }
+    // h_c fragment rows: row p = pt*32 + l32, swizzle of that row
+    const int hsw = swz<HRC>(l32);   // pt*32 leaves the swizzle unchanged
+
     if (nh > 0) store_vec(0);
     wait_vmem();
     __syncthreads();
@@ -323,23 +226,138 @@ __global__ __launch_bounds__(kScanThreads) __attribute__((amdgpu_waves_per_eu(1,
             if (NBH == 2 && c > 0) issue_h(hh + 1, buf ^ 1);
             load_vec(hh + 1);
         }
-        HeadView<T, ST> v;
-        v.xt = reinterpret_cast<const T*>(smem + xbi * XB);
-        v.ht = reinterpret_cast<const ST*>(hb0 + hbi * Cfg::HBYTES);
-        v.c2 = vb0 + buf * (VB / 4);
-        v.dt = v.c2 + Q;
-        v.ecs = v.c2 + 2 * Q;
-        v.u = v.c2 + 3 * Q;
-        const float Dh = ldg(p.D + h0 + hh);
-        T* yh = ybase + (int64_t)hh * P;
-        if (rs >= 0)
-            row_tile_head<T, PT, KS, Cfg::XRC, Cfg::HRC, 3, ST>(cb_s, cbd_s, cs_reg, v, rs, c > 0, Dh, yh, ystride, qc,
-                                                                (int)P, lane);
-        if (rl >= 0)
-            row_tile_head<T, PT, KS, Cfg::XRC, Cfg::HRC, 7, ST>(cb_l, cbd_l, cl_reg, v, rl, c > 0, Dh, yh, ystride, qc,
-                                                                (int)P, lane);
+        bool stored_all = true;
+        if (active) {
+            const unsigned char* xt = smem + xbi * XB;
+            const unsigned char* ht = hb0 + hbi * Cfg::HBYTES;
+            const float* c2v = vb0 + buf * (VB / 4);
+            const float* dtv = c2v + Q;
+            const float* ecs = c2v + 2 * Q;
+            const float* uv = c2v + 3 * Q;
+            int jl = rt * 32 + l32, qch = qc;
+            asm volatile("" : "+v"(jl), "+v"(qch));    // keep per-element compares in the loop
+            f32x16 acc[PT];
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt) acc[pt] = zero16();
+
+            if (c > 0) {   // (C . h_c), rows then scaled by exp(cs_j)
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+                    for (int pt = 0; pt < PT; ++pt) {
+                        const int row = pt * 32 + l32;
+                        const int cbyte = (ks * 16 + hf * 8) * SSZ;   // 16 or 32 bytes
+                        const unsigned char* rp = ht + row * HRC * 16;
+                        typename Vec8<ST>::type hv;
+                        if constexpr (SSZ == 2) {
+                            hv = *reinterpret_cast<const bf16x8*>(rp + ((((cbyte >> 4)) ^ hsw) << 4));
+                        } else {
+                            const f32x4 lo = *reinterpret_cast<const f32x4*>(rp + (((cbyte >> 4) ^ hsw) << 4));
+                            const f32x4 hi = *reinterpret_cast<const f32x4*>(rp + ((((cbyte >> 4) + 1) ^ hsw) << 4));
+                            hv[0] = lo[0]; hv[1] = lo[1]; hv[2] = lo[2]; hv[3] = lo[3];
+                            hv[4] = hi[0]; hv[5] = hi[1]; hv[6] = hi[2]; hv[7] = hi[3];
+                        }
+                        mma_k16(acc[pt], creg[ks], cvt8<T>(hv));
+                    }
+                }
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    const f32x4 e4 = *reinterpret_cast<const f32x4*>(ecs + rt * 32 + 8 * gq + 4 * hf);
+#pragma unroll
+                    for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) acc[pt][4 * gq + r] *= e4[r];
+                }
+            }
+
+            const float c2j = c2v[jl];
+            // key tiles off the diagonal: M = CB * exp(cs_j - cs_r) * u_i, no mask
+#pragma unroll
+            for (int kt = 0; kt < 7; ++kt) {
+                if (kt < rt) {
+                    const float vj = exp2f(c2j - c2v[kt * 32 + 31]);
+                    V8 aop[2];
+#pragma unroll
+                    for (int gq = 0; gq < 4; ++gq) {
+                        const f32x4 u4 = *reinterpret_cast<const f32x4*>(uv + kt * 32 + 8 * gq + 4 * hf);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int idx = 4 * gq + r;
+                            aop[idx >> 3][idx & 7] = from_f32<T>(to_f32(cb[kt][idx >> 3][idx & 7]) * vj * u4[r]);
+                        }
+                    }
+#pragma unroll
+                    for (int s = 0; s < 2; ++s)
+#pragma unroll
+                        for (int pt = 0; pt < PT; ++pt)
+                            mma_k16(acc[pt], aop[s], x_frag<T, XRC>(xt, 2 * kt + s, pt, xoa, xob, lane));
+                }
+            }
+            // the diagonal tile: direct decay; the causal mask (i <= j) enters as a
+            // -inf exponent for i > j, so exp2 gives exactly 0 with no lane masks
+            V8 xd[PT][2];
+            {
+                V8 aop[2];
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    const int ib = rt * 32 + 8 * gq + 4 * hf;
+                    const f32x4 ci = *reinterpret_cast<const f32x4*>(c2v + ib);
+                    const f32x4 di = *reinterpret_cast<const f32x4*>(dtv + ib);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int idx = 4 * gq + r;
+                        const float pen = __int_as_float(((jl - (ib + r)) >> 31) & (int)0xff800000u);
+                        const float m = to_f32(cbd[idx >> 3][idx & 7]) * exp2f((c2j - ci[r]) + pen) * di[r];
+                        aop[idx >> 3][idx & 7] = from_f32<T>(m);
+                    }
+                }
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+#pragma unroll
+                    for (int pt = 0; pt < PT; ++pt) {
+                        xd[pt][s] = x_frag<T, XRC>(xt, 2 * rt + s, pt, xoa, xob, lane);
+                        mma_k16(acc[pt], aop[s], xd[pt][s]);
+                    }
+            }
+
+            // epilogue: y = acc + D x_j, staged through this wave's LDS slab
+            // (8 rows at a time: accumulator quarter gq holds rows 8gq + 4hf + r)
+            // and written as 16-byte row segments
+            const float Dh = ldg(p.D + h0 + hh);
+            unsigned char* yh = ybase + (int64_t)hh * P * ESZ;
+            const uint32_t ystride = (uint32_t)(H * P * ESZ);
+            constexpr int RB = PT * 32 * ESZ;                   // staged row bytes
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+#pragma unroll
+                for (int pt = 0; pt < PT; ++pt) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int e = 4 * (gq & 1) + r;
+                        *reinterpret_cast<T*>(yst + (4 * hf + r) * RB + (pt * 32 + l32) * ESZ) =
+                            from_f32<T>(acc[pt][4 * gq + r] + Dh * to_f32(xd[pt][gq >> 1][e]));
+                    }
+                }
+#pragma unroll
+                for (int k = 0; k < Cfg::NSTORE; ++k) {
+                    const int idx = k * 64 + lane;
+                    const int jr = idx / (RB / 16), cb16 = idx % (RB / 16);
+                    const u32x4 val = *reinterpret_cast<const u32x4*>(yst + (idx < Cfg::YCHUNKS ? idx : 0) * 16);
+                    const int j = rt * 32 + 8 * gq + jr;
+                    if (idx < Cfg::YCHUNKS && j < qch && cb16 * 16 < (int)(P * ESZ))
+                        *(__attribute__((address_space(1))) u32x4*)(yh + (uint32_t)j * ystride + cb16 * 16) = val;
+                    else if (idx < Cfg::YCHUNKS)
+                        stored_all = false;
+                }
+            }
+        }
         if (more) store_vec(buf ^ 1);
-        wait_vmem();
+        // the next head's copies were issued before this head's stores: wait
+        // for everything but the stores just issued (all lanes stored) or all
+        if (__builtin_amdgcn_readfirstlane(__any(!stored_all) ? 1 : 0) == 0 && active)
+            wait_vmem_le<4 * Cfg::NSTORE>();
+        else
+            wait_vmem();
         __syncthreads();
         if (more && (NBX == 1 || (NBH == 1 && c > 0))) {   // single-buffered tiles
             if (NBX == 1) issue_x(hh + 1, 0);
@@ -407,7 +425,7 @@ hipError_t launch_chunk_scan(const Params& p, int dtype, int state_dtype, hipStr
 int chunk_scan_lds_bytes(int dtype, int state_dtype, int64_t P, int64_t N, int64_t Q) {
     const int esz = dtype == 1 ? 2 : 4, ssz = state_dtype == 1 ? 2 : 4;
     const int pp = (int)((P + 31) / 32) * 32, np = (int)((N + 31) / 32) * 32;
-    return (int)Q * pp * esz + pp * np * ssz + 2 * 4 * (int)Q * 4;
+    return (int)Q * pp * esz + pp * np * ssz + 2 * 4 * (int)Q * 4 + kScanWaves * 8 * pp * esz;
 }
 
 }  // namespace ssd

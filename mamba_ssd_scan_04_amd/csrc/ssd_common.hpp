@@ -256,4 +256,34 @@ template <typename T> __device__ __forceinline__ typename Vec8<T>::type cvt8(con
     return o;
 }
 
+
+// Two transpose reads at precomputed per-lane byte offsets (see frag_tr): the
+// k rows of a fragment step by whole 16-row groups, which leaves the swizzle
+// unchanged, so a fragment at row offset R is base + off + R * row_bytes.
+__device__ __forceinline__ bf16x8 frag_tr_at(const unsigned char* base, int off_a, int off_b) {
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + off_a));
+    const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + off_b));
+    const bf16x4 av = __builtin_bit_cast(bf16x4, a);
+    const bf16x4 bv = __builtin_bit_cast(bf16x4, b);
+    return __builtin_shufflevector(av, bv, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Lane byte offsets of the two transpose reads of frag_tr for rows
+// rowk(hf, e) (evaluated at the first 16-row group) and column tile col0.
+template <int RC, typename RowK>
+__device__ __forceinline__ void frag_tr_offsets(int col0, RowK rowk, int lane, int& off_a, int& off_b) {
+    const int q = lane >> 4, s = (lane >> 2) & 3, j = lane & 3, hf = lane >> 5;
+    const int cb = (col0 + 16 * (q & 1) + 4 * j) * 2;
+    off_a = tile_byte<RC>(rowk(hf, s), cb);
+    off_b = tile_byte<RC>(rowk(hf, s + 4), cb);
+}
+
+// Wait until at most N of this wavefront's vector memory operations are
+// outstanding (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
 }  // namespace ssd
