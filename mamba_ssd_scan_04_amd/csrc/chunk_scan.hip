@@ -82,12 +82,13 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
     const int64_t T_ = p.seqlen, H = p.nheads, P = p.headdim, N = p.dstate, G = p.ngroups;
     const int64_t hpg = p.heads_per_group, nc = p.nchunks;
     const int nhb = (int)((hpg + hpw - 1) / hpw);
-    int bx = blockIdx.x;
+    const int lin = xcd_logical_block();
+    int bx = lin % (int)gridDim.x;
     const int hb = bx % nhb;
     bx /= nhb;
     const int64_t g = bx % G;
     const int c = (int)(bx / G);
-    const int64_t b = blockIdx.y;
+    const int64_t b = lin / (int)gridDim.x;
     const int64_t h0 = g * hpg + (int64_t)hb * hpw;
     const int nh = (int)min<int64_t>(hpw, hpg - (int64_t)hb * hpw);
     const int64_t t0 = (int64_t)c * Q;
@@ -275,7 +276,7 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
 #pragma unroll
             for (int kt = 0; kt < 7; ++kt) {
                 if (kt < rt) {
-                    const float vj = exp2f(c2j - c2v[kt * 32 + 31]);
+                    const float vj = fast_exp2(c2j - c2v[kt * 32 + 31]);
                     V8 aop[2];
 #pragma unroll
                     for (int gq = 0; gq < 4; ++gq) {
@@ -307,7 +308,7 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
                     for (int r = 0; r < 4; ++r) {
                         const int idx = 4 * gq + r;
                         const float pen = __int_as_float(((jl - (ib + r)) >> 31) & (int)0xff800000u);
-                        const float m = to_f32(cbd[idx >> 3][idx & 7]) * exp2f((c2j - ci[r]) + pen) * di[r];
+                        const float m = to_f32(cbd[idx >> 3][idx & 7]) * fast_exp2((c2j - ci[r]) + pen) * di[r];
                         aop[idx >> 3][idx & 7] = from_f32<T>(m);
                     }
                 }

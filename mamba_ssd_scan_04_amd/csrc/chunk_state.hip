@@ -39,36 +39,74 @@ struct StateCfg {
     static constexpr int XBYTES = kStateKB * XRC * 16;       // one head's x block
     static constexpr int BBYTES = kStateKB * BRC * 16;
     static constexpr int BUF = BBYTES + HPW * XBYTES;        // one pipeline buffer
-    static constexpr int LDS = 2 * BUF + HPW * 256 * 4;      // + w vectors (Q <= 256)
+    // ring of LDS blocks: three (two in flight while one is used) when two
+    // workgroups still fit in a CU's LDS, else two. Two resident workgroups per
+    // CU let one's stores and prologue overlap the other's copies and math.
+    static constexpr int NBUF = 2 * (3 * BUF + HPW * 256 * 4) <= 160 * 1024 ? 3 : 2;
+    static constexpr int LDS = NBUF * BUF + HPW * 256 * 4;   // + w vectors (Q <= 256)
+    static constexpr int NDB = (kStateKB * BRC / 64 + 3) / 4;  // B copy instructions per wave
+    static constexpr int NDX = (kStateKB * XRC / 64 + 3) / 4;  // x copy instructions per wave per head
 };
 
+// Lane byte offsets, relative to the block's first row, of the copies a
+// wavefront issues for a full 32-row tile (see dma_tile); -1 = no copy.
+template <int RC, int NI>
+__device__ __forceinline__ void dma_plan(int (&off)[NI], int valid_chunks, uint32_t row_stride, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int k = wave + 4 * i;
+        if (k * 64 < kStateKB * RC) {
+            const int P = k * 64 + lane, r = P / RC;
+            int c = (P % RC) ^ swz<RC>(r);
+            c = c < valid_chunks ? c : valid_chunks - 1;
+            off[i] = (int)((uint32_t)r * row_stride + 16u * (uint32_t)c);
+        } else {
+            off[i] = -1;
+        }
+    }
+}
+template <int NI>
+__device__ __forceinline__ void dma_issue(unsigned char* lds, const unsigned char* gbase, const int (&off)[NI],
+                                          int wave) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        if (off[i] >= 0)
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(gbase + off[i]),
+                                             (__attribute__((address_space(3))) void*)(lds + (wave + 4 * i) * 1024),
+                                             16, 0, 0);
+    }
+}
+
 template <typename T, int PT, int NT, typename ST>
-__global__ __launch_bounds__(256) void ssd_chunk_state_kernel(Params p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void ssd_chunk_state_kernel(Params p) {
     using Cfg = StateCfg<T, PT, NT>;
-    constexpr int HPW = Cfg::HPW, WPH = Cfg::WPH, PTW = Cfg::PTW, NP = NT * 32;
+    using V8 = typename Vec8<T>::type;
+    constexpr int HPW = Cfg::HPW, WPH = Cfg::WPH, PTW = Cfg::PTW;
+    constexpr int ESZ = (int)sizeof(T);
     __shared__ __attribute__((aligned(1024))) unsigned char smem[Cfg::LDS];
-    float* wv = reinterpret_cast<float*>(smem + 2 * Cfg::BUF);   // [HPW][Q]
+    constexpr int NBUF = Cfg::NBUF;
+    float* wv = reinterpret_cast<float*>(smem + NBUF * Cfg::BUF);   // [HPW][Q]
 
     const int Q = (int)p.chunk;
     const int64_t T_ = p.seqlen, H = p.nheads, P = p.headdim, N = p.dstate, G = p.ngroups;
     const int64_t hpg = p.heads_per_group, nc = p.nchunks;
     const int nhb = (int)((hpg + HPW - 1) / HPW);
-    int bx = blockIdx.x;
+    const int lin = xcd_logical_block();
+    int bx = lin % (int)gridDim.x;
     const int hb = bx % nhb;
     bx /= nhb;
     const int64_t g = bx % G;
     const int c = (int)(bx / G);
-    const int64_t b = blockIdx.y;
+    const int64_t b = lin / (int)gridDim.x;
     const int64_t h0 = g * hpg + (int64_t)hb * HPW;
     const int nh = (int)min<int64_t>(HPW, hpg - (int64_t)hb * HPW);
     const int64_t t0 = (int64_t)c * Q;
     const int qc = (int)min<int64_t>(Q, T_ - t0);
+    const int64_t tok0 = b * T_ + t0;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wavefront
     const int hf = lane >> 5, l32 = lane & 31;
-    const int64_t tok0 = b * T_ + t0;
-    constexpr int ESZ = (int)sizeof(T);
 
     // decay-to-chunk-end weights w_j for every head of the block
     const float* csbase = p.cs + ((b * H + h0) * nc + c) * Q;
@@ -87,81 +125,140 @@ __global__ __launch_bounds__(256) void ssd_chunk_state_kernel(Params p) {
     const unsigned char* xbase = static_cast<const unsigned char*>(p.x) + (tok0 * H + h0) * P * ESZ;
     const uint32_t bstride = (uint32_t)(G * N * ESZ), xstride = (uint32_t)(H * P * ESZ);
     const int xvalid = (int)(P * ESZ / 16), bvalid = (int)(N * ESZ / 16);
+    int offb[Cfg::NDB], offx[Cfg::NDX];
+    dma_plan<Cfg::BRC, Cfg::NDB>(offb, bvalid, bstride, wave, lane);
+    dma_plan<Cfg::XRC, Cfg::NDX>(offx, xvalid, xstride, wave, lane);
     auto issue = [&](int blk, int buf) {
         unsigned char* base = smem + buf * Cfg::BUF;
-        // rows of the block past the chunk's last token re-read that token (their
-        // weight w is 0); a block wholly past it reads only that token
-        const int r0 = min(blk * kStateKB, qc - 1);
-        const int vrows = min(kStateKB, qc - r0);
-        dma_tile<Cfg::BRC>(base, kStateKB, vrows, bvalid, bbase + (uint32_t)r0 * bstride, bstride, wave, 4, lane);
-        for (int hq = 0; hq < nh; ++hq)
-            dma_tile<Cfg::XRC>(base + Cfg::BBYTES + hq * Cfg::XBYTES, kStateKB, vrows, xvalid,
-                               xbase + (uint32_t)r0 * xstride + (int64_t)hq * P * ESZ, xstride, wave, 4, lane);
+        const int r0 = blk * kStateKB;
+        if (r0 + kStateKB <= qc) {          // full block: precomputed lane offsets
+            dma_issue<Cfg::NDB>(base, bbase + (uint32_t)r0 * bstride, offb, wave);
+            for (int hq = 0; hq < nh; ++hq)
+                dma_issue<Cfg::NDX>(base + Cfg::BBYTES + hq * Cfg::XBYTES,
+                                    xbase + (uint32_t)r0 * xstride + (int64_t)hq * P * ESZ, offx, wave);
+        } else {
+            // rows past the chunk's last token re-read that token (their weight
+            // w is 0); a block wholly past it reads only that token
+            const int rb = min(r0, qc - 1);
+            const int vrows = min(kStateKB, qc - rb);
+            dma_tile<Cfg::BRC>(base, kStateKB, vrows, bvalid, bbase + (uint32_t)rb * bstride, bstride, wave, 4, lane);
+            for (int hq = 0; hq < nh; ++hq)
+                dma_tile<Cfg::XRC>(base + Cfg::BBYTES + hq * Cfg::XBYTES, kStateKB, vrows, xvalid,
+                                   xbase + (uint32_t)rb * xstride + (int64_t)hq * P * ESZ, xstride, wave, 4, lane);
+        }
     };
 
     const int hh = wave / WPH;           // this wavefront's head within the block
     const int pt0 = (wave % WPH) * PTW;  // its first p tile
     const bool active = hh < nh;
+    // transpose-read lane offsets (k rows 8hf + e of the first 16-row group)
+    auto rowk0 = [](int hf_, int e) { return 8 * hf_ + e; };
+    int xoa[PTW], xob[PTW], boa[NT], bob[NT];
+#pragma unroll
+    for (int i = 0; i < PTW; ++i) frag_tr_offsets<Cfg::XRC>((pt0 + i) * 32, rowk0, lane, xoa[i], xob[i]);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) frag_tr_offsets<Cfg::BRC>(n * 32, rowk0, lane, boa[n], bob[n]);
+
     f32x16 acc[PTW][NT];
 #pragma unroll
     for (int i = 0; i < PTW; ++i)
 #pragma unroll
         for (int n = 0; n < NT; ++n) acc[i][n] = zero16();
 
+    // copies this wavefront issues per block (same set of instruction slots in
+    // the planned and the generic path)
+    int nb = 0, nx = 0;
+#pragma unroll
+    for (int i = 0; i < Cfg::NDB; ++i) nb += ((wave + 4 * i) * 64 < kStateKB * Cfg::BRC) ? 1 : 0;
+#pragma unroll
+    for (int i = 0; i < Cfg::NDX; ++i) nx += ((wave + 4 * i) * 64 < kStateKB * Cfg::XRC) ? 1 : 0;
+    const int per_block = nb + nh * nx;
+
     const int nblk = Q / kStateKB;
-    issue(0, 0);
-    wait_vmem();
+    constexpr int AHEAD = NBUF - 1;     // blocks in flight beyond the one in use
+    for (int k = 0; k < AHEAD && k < nblk; ++k) issue(k, k);
+    wait_vmem_le_rt(nblk > 1 && AHEAD > 1 ? per_block : 0);   // block 0 landed
     __syncthreads();
     for (int blk = 0; blk < nblk; ++blk) {
-        const int buf = blk & 1;
-        if (blk + 1 < nblk) issue(blk + 1, buf ^ 1);
+        const int buf = blk % NBUF;
+        if (blk + AHEAD < nblk) issue(blk + AHEAD, (blk + AHEAD) % NBUF);
         if (active) {
             const unsigned char* base = smem + buf * Cfg::BUF;
-            const T* btile = reinterpret_cast<const T*>(base);
-            const T* xtile = reinterpret_cast<const T*>(base + Cfg::BBYTES + hh * Cfg::XBYTES);
+            const unsigned char* xtile = base + Cfg::BBYTES + hh * Cfg::XBYTES;
             const float* wrow = wv + hh * Q + blk * kStateKB;
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-                auto rowk = [s](int hf_, int e) { return 16 * s + 8 * hf_ + e; };
+                const int rofs_x = 16 * s * Cfg::XRC * 16, rofs_b = 16 * s * Cfg::BRC * 16;
                 const f32x4 w0 = *reinterpret_cast<const f32x4*>(wrow + 16 * s + 8 * hf);
                 const f32x4 w1 = *reinterpret_cast<const f32x4*>(wrow + 16 * s + 8 * hf + 4);
-                typename Vec8<T>::type xf[PTW], bf[NT];
+                V8 xf[PTW], bf[NT];
 #pragma unroll
                 for (int i = 0; i < PTW; ++i) {
-                    const auto raw = frag_tr<Cfg::XRC>(xtile, (pt0 + i) * 32, rowk, lane);
+                    V8 raw;
+                    if constexpr (ESZ == 2) {
+                        raw = frag_tr_at(xtile + rofs_x, xoa[i], xob[i]);
+                    } else {
+                        auto rowk = [s](int hf_, int e) { return 16 * s + 8 * hf_ + e; };
+                        raw = frag_tr<Cfg::XRC>(reinterpret_cast<const T*>(xtile), (pt0 + i) * 32, rowk, lane);
+                    }
 #pragma unroll
                     for (int e = 0; e < 8; ++e)
                         xf[i][e] = from_f32<T>(to_f32(raw[e]) * (e < 4 ? w0[e] : w1[e - 4]));
                 }
 #pragma unroll
-                for (int n = 0; n < NT; ++n) bf[n] = frag_tr<Cfg::BRC>(btile, n * 32, rowk, lane);
+                for (int n = 0; n < NT; ++n) {
+                    if constexpr (ESZ == 2) {
+                        bf[n] = frag_tr_at(base + rofs_b, boa[n], bob[n]);
+                    } else {
+                        auto rowk = [s](int hf_, int e) { return 16 * s + 8 * hf_ + e; };
+                        bf[n] = frag_tr<Cfg::BRC>(reinterpret_cast<const T*>(base), n * 32, rowk, lane);
+                    }
+                }
+                // out[n][p]: B^T rows as the A operand, scaled x as the B operand,
+                // so each lane ends up holding 4 consecutive n of one p
 #pragma unroll
                 for (int i = 0; i < PTW; ++i)
 #pragma unroll
-                    for (int n = 0; n < NT; ++n) mma_k16(acc[i][n], xf[i], bf[n]);
+                    for (int n = 0; n < NT; ++n) mma_k16(acc[i][n], bf[n], xf[i]);
             }
         }
-        wait_vmem();
+        // block blk+1 must have landed; later blocks may still be in flight
+        const int later = min(AHEAD - 1, nblk - 2 - blk);
+        wait_vmem_le_rt(later > 0 ? later * per_block : 0);
         __syncthreads();
     }
 
     if (active) {
+        // accumulator element r of tile (i, n): state row p = (pt0+i)*32 + lane%32,
+        // column n*32 + 8*(r/4) + 4*hf + r%4: four consecutive n per store
         const int64_t h = h0 + hh;
         ST* sg = static_cast<ST*>(p.states) + ((b * nc + c) * H + h) * P * N;   // [P][N] of this head
 #pragma unroll
         for (int i = 0; i < PTW; ++i) {
+            const int pr = (pt0 + i) * 32 + l32;
 #pragma unroll
             for (int n = 0; n < NT; ++n) {
-                const int64_t col = n * 32 + l32;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int64_t pr = (pt0 + i) * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-                    if (pr < P && col < N) stg<ST>(sg + (uint32_t)(pr * N + col), from_f32<ST>(acc[i][n][r]));
+                for (int gq = 0; gq < 4; ++gq) {
+                    const int col = n * 32 + 8 * gq + 4 * hf;
+                    if (pr < P && col < N) {
+                        ST* dst = sg + (uint32_t)(pr * (int)N + col);
+                        if constexpr (sizeof(ST) == 4) {
+                            f32x4 v;
+                            v[0] = acc[i][n][4 * gq]; v[1] = acc[i][n][4 * gq + 1];
+                            v[2] = acc[i][n][4 * gq + 2]; v[3] = acc[i][n][4 * gq + 3];
+                            *(__attribute__((address_space(1))) f32x4*)dst = v;
+                        } else {
+                            bf16x4 v;
+                            v[0] = from_f32<bf16>(acc[i][n][4 * gq]); v[1] = from_f32<bf16>(acc[i][n][4 * gq + 1]);
+                            v[2] = from_f32<bf16>(acc[i][n][4 * gq + 2]); v[3] = from_f32<bf16>(acc[i][n][4 * gq + 3]);
+                            *(__attribute__((address_space(1))) bf16x4*)dst = v;
+                        }
+                    }
                 }
             }
         }
     }
-    (void)NP;
 }
 
 template <typename T, int PT, int NT, typename ST>

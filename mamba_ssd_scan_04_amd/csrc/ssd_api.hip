@@ -2,7 +2,7 @@
 // layout and the launch order of the four kernels. No allocation, no state.
 #include <stdint.h>
 
-#include "../../include/ssd.h"
+#include "ssd.h"
 #include "kernels.hpp"
 
 namespace ssd {

@@ -286,4 +286,35 @@ __device__ __forceinline__ void wait_vmem_le() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
+
+// Wait until at most n (0..31, runtime, wave-uniform) vector memory operations
+// of this wavefront are outstanding.
+__device__ __forceinline__ void wait_vmem_le_rt(int n) {
+    switch (n) {
+#define SSD_WAIT_CASE(K) case K: wait_vmem_le<K>(); break;
+        SSD_WAIT_CASE(0) SSD_WAIT_CASE(1) SSD_WAIT_CASE(2) SSD_WAIT_CASE(3) SSD_WAIT_CASE(4)
+        SSD_WAIT_CASE(5) SSD_WAIT_CASE(6) SSD_WAIT_CASE(7) SSD_WAIT_CASE(8) SSD_WAIT_CASE(9)
+        SSD_WAIT_CASE(10) SSD_WAIT_CASE(11) SSD_WAIT_CASE(12) SSD_WAIT_CASE(13) SSD_WAIT_CASE(14)
+        SSD_WAIT_CASE(15) SSD_WAIT_CASE(16) SSD_WAIT_CASE(17) SSD_WAIT_CASE(18) SSD_WAIT_CASE(19)
+        SSD_WAIT_CASE(20) SSD_WAIT_CASE(21) SSD_WAIT_CASE(22) SSD_WAIT_CASE(23) SSD_WAIT_CASE(24)
+        SSD_WAIT_CASE(25) SSD_WAIT_CASE(26) SSD_WAIT_CASE(27) SSD_WAIT_CASE(28) SSD_WAIT_CASE(29)
+        SSD_WAIT_CASE(30) SSD_WAIT_CASE(31)
+#undef SSD_WAIT_CASE
+        default: wait_vmem(); break;
+    }
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs (id % 8), each with
+// its own L2. Remap the linear id so that a contiguous range of logical
+// indices runs on one XCD: neighbouring logical blocks (same chunk, other
+// heads) then share B and C through the same L2.
+__device__ __forceinline__ int xcd_logical_block() {
+    const int total = (int)(gridDim.x * gridDim.y);
+    const int id = (int)(blockIdx.x + gridDim.x * blockIdx.y);
+    return (total % 8 == 0) ? (id % 8) * (total / 8) + id / 8 : id;
+}
+
+// 2^x on the hardware transcendental unit (v_exp_f32): results below the
+// smallest normal flush to 0, 2^-inf = 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 }  // namespace ssd
