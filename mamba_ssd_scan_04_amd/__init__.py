@@ -180,8 +180,14 @@ def alloc_workspace(d: SsdDims, device) -> torch.Tensor:
     return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
 
 
-def forward(x, dt, A, B, C, D, chunk_size: int, state_dtype: str = "fp32", workspace=None):
-    """y, final_state = SSD(x, dt, A, B, C, D) through ssd_forward."""
+def forward(x, dt, A, B, C, D, chunk_size: int, state_dtype: str | None = None, workspace=None):
+    """y, final_state = SSD(x, dt, A, B, C, D) through ssd_forward.
+
+    state_dtype is the storage of the inter-chunk states in the workspace
+    ("fp32" or "bf16"; default: that of x). The running state and the returned
+    final state are fp32 either way."""
+    if state_dtype is None:
+        state_dtype = "bf16" if x.dtype == torch.bfloat16 else "fp32"
     d = dims_of(x, B, chunk_size, state_dtype)
     _check(ssd_check_dims(d))
     y = torch.empty_like(x)
