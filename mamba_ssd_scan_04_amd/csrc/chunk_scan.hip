@@ -9,22 +9,29 @@
 //
 //   y_j = sum_{i<=j} (C_j . B_i) exp(cs_j - cs_i) dt_i x_i  +  exp(cs_j) C_j^T h_c  +  D x_j
 //
-// Work split. One workgroup of 8 wavefronts takes one chunk and `hpw` heads of
-// one group; wavefront w owns the 32-token row tile w (rows j), for every head.
+// Work split. One workgroup of 8 wavefronts takes one chunk and up to `hpw`
+// heads of one group (interleaved: heads h0, h0 + nhb, ...); wavefront w owns
+// the 32-token row tile w (rows j), for every head.
 //  Phase A, once per workgroup: C B^T does not depend on the head when B and C
 //  are shared (Knowl 7), so each wavefront computes its row of 32x32 tiles
-//  M^T(kt) = B_kt . C_w^T (kt <= w) on the matrix cores, rounds them to the
-//  operand type and keeps them in registers, together with its C rows.
+//  M^T(kt) = B_kt . C_w^T (kt <= w) on the matrix cores and rounds them to the
+//  operand type. The off-diagonal tiles go to LDS (or stay in registers when
+//  LDS is too small), the diagonal tile and the wave's C rows stay in
+//  registers.
 //  Phase B, per head: x (token-major) and h_c ([P][N]) are copied into LDS by
-//  global_load_lds, double-buffered so the next head's copy overlaps this
-//  head's math. For every key tile the lane scales its 16 register values by
-//  the decay (exp(cs_j - cs_r) * exp(cs_r - cs_i) dt_i with r the key tile's
-//  last token off the diagonal; a direct exp with the causal mask on it) and
-//  feeds them straight to Y += M . X as the A operand: an accumulator's rows
-//  (8g + 4hf + r) become the next product's k index in "fragment order", and
-//  the x fragment is read from LDS with transpose reads in the same order.
-//  The carried-state term is (C . h_c) with rows scaled by exp(cs_j).
-//  The epilogue adds D x_j and stores y (lane = column p).
+//  buffer loads straight to LDS, double-buffered so the next head's copy
+//  overlaps this head's math. The key tiles are processed as a pipeline of
+//  stages whose LDS operands are read one stage ahead. For every key tile the
+//  lane scales its 16 C B^T values by the decay (exp(cs_j - cs_r) *
+//  exp(cs_r - cs_i) dt_i with r the key tile's last token off the diagonal, the
+//  per-key factor arriving by a row broadcast; a direct exp with the causal
+//  mask on it) and feeds them straight to the next product as its M operand:
+//  an accumulator's rows (8g + 4hf + r) become the next product's k index in
+//  "fragment order", and the x fragment is read from LDS with transpose reads
+//  in the same order. The products are formed transposed (Y^T = X^T M^T), so
+//  each lane ends with 16 values of p for one token j. The carried-state term
+//  is (C . h_c) with rows scaled by exp(cs_j). The epilogue adds D x_j and
+//  stores y in 16-byte pieces of token rows.
 #include "kernels.hpp"
 
 namespace ssd {
@@ -40,14 +47,14 @@ struct ScanCfg {
     static constexpr int HRC = NT * 32 * (int)sizeof(ST) / 16; // chunks per h_c row
     static constexpr int HBYTES = PT * 32 * HRC * 16;          // one head's h_c tile
     static constexpr int KS = NT * 2;                          // k16 steps over n
-    static constexpr int YBYTES = 8 * PT * 32 * (int)sizeof(T);    // per-wave y staging: 8 rows
-    static constexpr int YCHUNKS = YBYTES / 16;                 // 16-byte row segments staged
-    static constexpr int NSTORE = (YCHUNKS + 63) / 64;          // store instructions per 8 rows
+    static constexpr int CBTILE = 2 * 64 * 8 * (int)sizeof(T);  // one 32x32 C B^T tile, lane-major
     __host__ __device__ static int xbytes(int Q) { return Q * XRC * 16; }
     __host__ __device__ static int vbytes(int Q) { return 4 * Q * 4; }
-    // bytes of LDS with nbx x buffers and nbh h_c buffers
-    __host__ __device__ static int lds(int Q, int nbx, int nbh) {
-        return nbx * xbytes(Q) + nbh * HBYTES + 2 * vbytes(Q) + kScanWaves * YBYTES;
+    // the off-diagonal C B^T tiles of all row tiles (kt < rt), when kept in LDS
+    __host__ __device__ static int cbbytes(int Q) { return (Q / 32) * (Q / 32 - 1) / 2 * CBTILE; }
+    // bytes of LDS with nbx x buffers, nbh h_c buffers and C B^T in LDS or not
+    __host__ __device__ static int lds(int Q, int nbx, int nbh, bool cbl) {
+        return nbx * xbytes(Q) + nbh * HBYTES + 2 * vbytes(Q) + (cbl ? cbbytes(Q) : 0);
     }
 };
 
@@ -65,7 +72,7 @@ __device__ __forceinline__ typename Vec8<T>::type x_frag(const unsigned char* xt
     }
 }
 
-template <typename T, int PT, int NT, typename ST, int NBX, int NBH>
+template <typename T, int PT, int NT, typename ST, int NBX, int NBH, bool CBL>
 __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, int hpw) {
     using Cfg = ScanCfg<T, PT, NT, ST>;
     using V8 = typename Vec8<T>::type;
@@ -76,7 +83,7 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
     const int XB = Cfg::xbytes(Q), VB = Cfg::vbytes(Q);
     unsigned char* const hb0 = smem + NBX * XB;
     float* const vb0 = reinterpret_cast<float*>(hb0 + NBH * Cfg::HBYTES);
-    unsigned char* const yst0 = reinterpret_cast<unsigned char*>(vb0) + 2 * VB;
+    unsigned char* const cbl0 = reinterpret_cast<unsigned char*>(vb0) + 2 * VB;   // C B^T tiles (CBL)
 
     // ---- block coordinates (uniform) ----
     const int64_t T_ = p.seqlen, H = p.nheads, P = p.headdim, N = p.dstate, G = p.ngroups;
@@ -89,8 +96,12 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
     const int64_t g = bx % G;
     const int c = (int)(bx / G);
     const int64_t b = lin / (int)gridDim.x;
-    const int64_t h0 = g * hpg + (int64_t)hb * hpw;
-    const int nh = (int)min<int64_t>(hpw, hpg - (int64_t)hb * hpw);
+    // this workgroup's heads of the group: h0 + hh * nhb, hh < nh. Interleaved
+    // (not consecutive) so that the workgroups of one chunk, running side by
+    // side, read and write neighbouring heads' 128-byte row pieces together.
+    const int64_t h0 = g * hpg + hb;
+    const int nh = (int)((hpg - hb + nhb - 1) / nhb);
+    const int64_t hs = nhb;
     const int64_t t0 = (int64_t)c * Q;
     const int qc = (int)min<int64_t>(Q, T_ - t0);
     const int64_t tok0 = b * T_ + t0;            // first token row of the chunk
@@ -103,7 +114,6 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
     const int RT = Q / 32;
     const int rt = RT == 8 ? (wave < 4 ? wave : 11 - wave) : (wave < RT ? wave : -1);
     const bool active = rt >= 0;
-    unsigned char* const yst = yst0 + wave * Cfg::YBYTES;
 
     const uint32_t bcs = (uint32_t)(G * N);
     const T* cbase = static_cast<const T*>(p.C) + (tok0 * G + g) * N;
@@ -116,47 +126,62 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
     const float* dtbase = p.dt + tok0 * H + h0;
     const int xvalid = (int)(P * ESZ / 16), hvalid = (int)(N * SSZ / 16);
 
-    auto issue_x = [&](int hh, int buf) {
-        dma_tile<XRC>(smem + buf * XB, Q, qc, xvalid, xbase + (int64_t)hh * P * ESZ, xstride, wave, kScanWaves, lane);
+    // tile copies: lane offsets planned once, the same for every head
+    constexpr int NIX = (256 * XRC / 64 + kScanWaves - 1) / kScanWaves;
+    constexpr int NIH = (PT * 32 * HRC / 64 + kScanWaves - 1) / kScanWaves;
+    int offx[NIX], offh[NIH];
+    dma_tile_plan<XRC, NIX>(offx, Q, qc, xvalid, xstride, wave, kScanWaves, lane);
+    dma_tile_plan<HRC, NIH>(offh, PT * 32, (int)P, hvalid, (uint32_t)(N * SSZ), wave, kScanWaves, lane);
+    auto issue_x = [&](int hh, unsigned char* dst) {
+        dma_tile_issue<NIX>(dst, xbase + (int64_t)hh * hs * P * ESZ, offx, wave, kScanWaves);
     };
-    auto issue_h = [&](int hh, int buf) {
-        dma_tile<HRC>(hb0 + buf * Cfg::HBYTES, PT * 32, (int)P, hvalid, sbase + (int64_t)hh * P * N * SSZ,
-                      (uint32_t)(N * SSZ), wave, kScanWaves, lane);
+    auto issue_h = [&](int hh, unsigned char* dst) {
+        dma_tile_issue<NIH>(dst, sbase + (int64_t)hh * hs * P * N * SSZ, offh, wave, kScanWaves);
     };
     float vcs = 0.0f, vcr = 0.0f, vdt = 0.0f;   // thread i holds token i of the next head
     auto load_vec = [&](int hh) {
         const int i = threadIdx.x;
         if (i < Q) {
-            const float* csr = csbase + (int64_t)hh * nc * Q;
+            const float* csr = csbase + (int64_t)hh * hs * nc * Q;
             vcs = ldg(csr + i);
             vcr = ldg(csr + (i | 31));
-            vdt = (i < qc) ? ldg(dtbase + hh + (uint32_t)i * (uint32_t)H) : 0.0f;
+            vdt = (i < qc) ? ldg(dtbase + hh * hs + (uint32_t)i * (uint32_t)H) : 0.0f;
         }
     };
-    auto store_vec = [&](int buf) {
+    // per-head vectors in LDS, token i of the chunk (log2 units: c2 = cs log2 e):
+    //   [0, Q)   c2_i
+    //   [Q, 2Q)  2^c2_i                          (carried-state row scale)
+    //   [2Q,3Q)  2^(c2_r - c2_i) dt_i, r = the last token of i's 32-token tile
+    //   [3Q,4Q)  dt_i                            (0 past the chunk's end)
+    auto store_vec = [&](float* v) {
         const int i = threadIdx.x;
         if (i < Q) {
-            float* v = vb0 + buf * (VB / 4);
             const float c2 = vcs * kLog2e, c2r = vcr * kLog2e;
             v[i] = c2;
-            v[Q + i] = vdt;
-            v[2 * Q + i] = exp2f(c2);
-            v[3 * Q + i] = exp2f(c2r - c2) * vdt;
+            v[Q + i] = exp2f(c2);
+            v[2 * Q + i] = exp2f(c2r - c2) * vdt;
+            v[3 * Q + i] = vdt;
         }
     };
 
+    // D of this workgroup's heads, lane l holding head h0 + l nhb (read per head
+    // with a lane broadcast, so no scalar loads sit in the head loop)
+    const float dlane = ldg(p.D + h0 + (lane < nh ? lane : 0) * hs);
     // head 0's tiles start moving before phase A
     if (nh > 0) {
-        issue_x(0, 0);
-        if (c > 0) issue_h(0, 0);
         load_vec(0);
+        issue_x(0, smem);
+        if (c > 0) issue_h(0, hb0);
     }
 
     // ---- phase A: this wave's C rows and C B^T row of tiles, once per workgroup ----
     const int nlast = (int)N - 8;
     V8 creg[KS];
-    V8 cb[7][2];     // key tiles kt < rt
-    V8 cbd[2];       // the diagonal tile
+    V8 cb[CBL ? 1 : 7][2];   // key tiles kt < rt, in registers unless kept in LDS
+    V8 cbd[2];               // the diagonal tile
+    // this row tile's off-diagonal tiles in LDS: tile kt at cbw + kt * CBTILE,
+    // lane l's 8 low / 8 high elements at l * 8 and (64 + l) * 8 elements
+    unsigned char* const cbw = cbl0 + (rt > 0 ? rt * (rt - 1) / 2 : 0) * Cfg::CBTILE;
     if (active) {
         auto off = [&](int row, int ks) {
             return (uint32_t)min(row, qc - 1) * bcs + (uint32_t)min(ks * 16 + hf * 8, nlast);
@@ -191,8 +216,13 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
                     hi[e] = from_f32<T>(acc[8 + e]);
                 }
                 if (kt < rt) {
-                    cb[kt < 7 ? kt : 6][0] = lo;
-                    cb[kt < 7 ? kt : 6][1] = hi;
+                    if constexpr (CBL) {
+                        store8(reinterpret_cast<T*>(cbw + kt * Cfg::CBTILE) + lane * 8, lo);
+                        store8(reinterpret_cast<T*>(cbw + kt * Cfg::CBTILE) + (64 + lane) * 8, hi);
+                    } else {
+                        cb[kt < 7 ? kt : 6][0] = lo;
+                        cb[kt < 7 ? kt : 6][1] = hi;
+                    }
                 } else {
                     cbd[0] = lo;
                     cbd[1] = hi;
@@ -212,166 +242,254 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
     // h_c fragment rows: row p = pt*32 + l32, swizzle of that row
     const int hsw = swz<HRC>(l32);   // pt*32 leaves the swizzle unchanged
 
-    if (nh > 0) store_vec(0);
+    if (nh > 0) store_vec(vb0);
     wait_vmem();
     __syncthreads();
 
     // ---- phase B: heads ----
-    for (int hh = 0; hh < nh; ++hh) {
-        const int buf = hh & 1;
-        const int xbi = NBX == 2 ? buf : 0;
-        const int hbi = NBH == 2 ? buf : 0;
+    // One head: start the copies of the next head's tiles into xn / hn (when
+    // double-buffered) and its vectors, compute this head from xt / ht / c2v,
+    // store y, and write the next head's vectors into vn. The LDS regions are passed as non-aliasing pointers so that the
+    // compiler knows this head's LDS reads do not depend on the copies in
+    // flight and does not wait for them (they are waited for explicitly at the
+    // end of the head). Returns false if some lane skipped a y store.
+    // Operands of one 32-token key tile of the masked product, read from LDS
+    // one step ahead of their use: the C B^T tile (off the diagonal), the
+    // key tile's last c2, x fragments, and per-key vectors held one value per
+    // lane in row-broadcast order (lane 16q + n holds key token
+    // 8(n/4) + 4(q/2) + n%4 of the tile, which is accumulator element n of
+    // every lane of that row's half): u off the diagonal, c2 and dt on it.
+    struct Stage {
+        V8 m[2];
+        float u, d, r;
+        V8 xf[2][PT];
+    };
+    const int bcl = 8 * ((lane & 15) >> 2) + 4 * (lane >> 5) + (lane & 3);   // key token of this lane's slot
+    auto head = [&](int hh, const unsigned char* __restrict__ xt, const unsigned char* __restrict__ ht,
+                    const float* __restrict__ c2v, const unsigned char* __restrict__ cbt,
+                    unsigned char* __restrict__ xn, unsigned char* __restrict__ hn,
+                    float* __restrict__ vn, float Dh) __attribute__((always_inline)) {
         const bool more = hh + 1 < nh;
         if (more) {
-            if (NBX == 2) issue_x(hh + 1, buf ^ 1);
-            if (NBH == 2 && c > 0) issue_h(hh + 1, buf ^ 1);
-            load_vec(hh + 1);
+            load_vec(hh + 1);   // before the copies: its results are waited for without them
+            if (NBX == 2) issue_x(hh + 1, xn);
+            if (NBH == 2 && c > 0) issue_h(hh + 1, hn);
         }
         bool stored_all = true;
         if (active) {
-            const unsigned char* xt = smem + xbi * XB;
-            const unsigned char* ht = hb0 + hbi * Cfg::HBYTES;
-            const float* c2v = vb0 + buf * (VB / 4);
-            const float* dtv = c2v + Q;
-            const float* ecs = c2v + 2 * Q;
-            const float* uv = c2v + 3 * Q;
+            const float* ecs = c2v + Q;
+            const float* uv = c2v + 2 * Q;
+            const float* dtv = c2v + 3 * Q;
             int jl = rt * 32 + l32, qch = qc;
             asm volatile("" : "+v"(jl), "+v"(qch));    // keep per-element compares in the loop
+            // The products are formed transposed, Y^T = X^T M^T (+ h^T C^T): the
+            // same registers as Y = M X with the A and B operands swapped, which
+            // leaves each lane holding 16 values of p for one token j.
             f32x16 acc[PT];
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt) acc[pt] = zero16();
+            const float c2j = c2v[jl];
+            const float ej = ecs[jl];
 
-            if (c > 0) {   // (C . h_c), rows then scaled by exp(cs_j)
+            // stage k < rt: off-diagonal key tile k; k == rt: the diagonal tile.
+            // Every stage issues the same LDS reads whatever k is (addresses are
+            // selected, not branched over, and k is clamped to rt), so that the
+            // number of reads in flight is known where each stage's data is
+            // waited for and the wait covers only that stage's reads.
+            auto load_stage = [&](Stage& st, int k) __attribute__((always_inline)) {
+                k = k < rt ? k : rt;
+                const bool off = k < rt;
+                if constexpr (CBL) {
+                    const unsigned char* mp = off ? cbt + k * Cfg::CBTILE : xt;   // xt: any readable LDS
+                    st.m[0] = load8(reinterpret_cast<const T*>(mp) + lane * 8);
+                    st.m[1] = load8(reinterpret_cast<const T*>(mp) + (64 + lane) * 8);
+                } else {
+                    st.m[0] = cb[CBL ? 0 : (k < 7 ? k : 6)][0];
+                    st.m[1] = cb[CBL ? 0 : (k < 7 ? k : 6)][1];
+                }
+                st.r = c2v[k * 32 + 31];
+                st.u = (off ? uv : c2v)[k * 32 + bcl];
+                st.d = dtv[k * 32 + bcl];
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
+                for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-                    for (int pt = 0; pt < PT; ++pt) {
-                        const int row = pt * 32 + l32;
-                        const int cbyte = (ks * 16 + hf * 8) * SSZ;   // 16 or 32 bytes
-                        const unsigned char* rp = ht + row * HRC * 16;
-                        typename Vec8<ST>::type hv;
-                        if constexpr (SSZ == 2) {
-                            hv = *reinterpret_cast<const bf16x8*>(rp + ((((cbyte >> 4)) ^ hsw) << 4));
-                        } else {
-                            const f32x4 lo = *reinterpret_cast<const f32x4*>(rp + (((cbyte >> 4) ^ hsw) << 4));
-                            const f32x4 hi = *reinterpret_cast<const f32x4*>(rp + ((((cbyte >> 4) + 1) ^ hsw) << 4));
-                            hv[0] = lo[0]; hv[1] = lo[1]; hv[2] = lo[2]; hv[3] = lo[3];
-                            hv[4] = hi[0]; hv[5] = hi[1]; hv[6] = hi[2]; hv[7] = hi[3];
+                    for (int pt = 0; pt < PT; ++pt) st.xf[s2][pt] = x_frag<T, XRC>(xt, 2 * k + s2, pt, xoa, xob, lane);
+            };
+            // off the diagonal M = CB 2^(c2_j - c2_r) u_i, no mask; on it
+            // M = CB 2^(c2_j - c2_i) dt_i (the difference is exact for i = j),
+            // with the causal mask (i <= j) entering as a -inf exponent for
+            // i > j (exp2 gives exactly 0)
+            auto run_stage = [&](const Stage& st, int k) __attribute__((always_inline)) {
+                V8 aop[2];
+                if (k < rt) {
+                    const float vj = fast_exp2(c2j - st.r);
+                    static_for<16>([&](auto I) {
+                        constexpr int idx = decltype(I)::value;
+                        aop[idx >> 3][idx & 7] =
+                            from_f32<T>(row_bcast<idx>(st.u) * (to_f32(st.m[idx >> 3][idx & 7]) * vj));
+                    });
+                } else {
+                    const int dj = jl - (k * 32 + 4 * hf);   // element idx is causal iff 8(idx/4) + idx%4 <= dj
+                    static_for<16>([&](auto I) {
+                        constexpr int idx = decltype(I)::value;
+                        constexpr int off = 8 * (idx >> 2) + (idx & 3);
+                        const float pen = __int_as_float(((dj - off) >> 31) & (int)0xff800000u);
+                        aop[idx >> 3][idx & 7] = from_f32<T>(
+                            to_f32(cbd[idx >> 3][idx & 7]) * fast_exp2((c2j - row_bcast<idx>(st.u)) + pen) *
+                            row_bcast<idx>(st.d));
+                    });
+                }
+#pragma unroll
+                for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                    for (int pt = 0; pt < PT; ++pt) mma_k16(acc[pt], st.xf[s2][pt], aop[s2]);
+            };
+
+            // ping-pong stages: the operands of stage k+1 are read (all of
+            // them issued) before stage k computes; the scheduling barriers
+            // keep the compiler from sinking those reads into their uses
+            Stage sa, sb;
+            if (c > 0) {   // (h_c^T C^T), then scaled by exp(cs_j)
+                typename Vec8<ST>::type hv[KS / 2][PT];
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+#pragma unroll
+                    for (int k2 = 0; k2 < KS / 2; ++k2) {
+                        const int ks = half * (KS / 2) + k2;
+#pragma unroll
+                        for (int pt = 0; pt < PT; ++pt) {
+                            const int cbyte = (ks * 16 + hf * 8) * SSZ;   // 16 or 32 bytes
+                            const unsigned char* rp = ht + (pt * 32 + l32) * HRC * 16;
+                            if constexpr (SSZ == 2) {
+                                hv[k2][pt] = *reinterpret_cast<const bf16x8*>(rp + (((cbyte >> 4) ^ hsw) << 4));
+                            } else {
+                                const f32x4 lo = *reinterpret_cast<const f32x4*>(rp + (((cbyte >> 4) ^ hsw) << 4));
+                                const f32x4 hi = *reinterpret_cast<const f32x4*>(rp + ((((cbyte >> 4) + 1) ^ hsw) << 4));
+                                hv[k2][pt][0] = lo[0]; hv[k2][pt][1] = lo[1]; hv[k2][pt][2] = lo[2]; hv[k2][pt][3] = lo[3];
+                                hv[k2][pt][4] = hi[0]; hv[k2][pt][5] = hi[1]; hv[k2][pt][6] = hi[2]; hv[k2][pt][7] = hi[3];
+                            }
                         }
-                        mma_k16(acc[pt], creg[ks], cvt8<T>(hv));
                     }
+                    if (half == 1) load_stage(sa, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int k2 = 0; k2 < KS / 2; ++k2)
+#pragma unroll
+                        for (int pt = 0; pt < PT; ++pt) mma_k16(acc[pt], cvt8<T>(hv[k2][pt]), creg[half * (KS / 2) + k2]);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
 #pragma unroll
-                for (int gq = 0; gq < 4; ++gq) {
-                    const f32x4 e4 = *reinterpret_cast<const f32x4*>(ecs + rt * 32 + 8 * gq + 4 * hf);
+                for (int pt = 0; pt < PT; ++pt)
 #pragma unroll
-                    for (int pt = 0; pt < PT; ++pt)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) acc[pt][4 * gq + r] *= e4[r];
-                }
+                    for (int r = 0; r < 16; ++r) acc[pt][r] *= ej;
+            } else {
+                load_stage(sa, 0);
+            }
+            // stages 0 .. rt (rt + 1 of them), two per iteration; the reads
+            // past stage rt repeat stage rt's and go unused
+            for (int k = 0; k <= rt; k += 2) {
+                load_stage(sb, k + 1);
+                __builtin_amdgcn_sched_barrier(0);
+                run_stage(sa, k);
+                __builtin_amdgcn_sched_barrier(0);
+                load_stage(sa, k + 2);
+                __builtin_amdgcn_sched_barrier(0);
+                if (k + 1 <= rt) run_stage(sb, k + 1);
+                __builtin_amdgcn_sched_barrier(0);
             }
 
-            const float c2j = c2v[jl];
-            // key tiles off the diagonal: M = CB * exp(cs_j - cs_r) * u_i, no mask
+            // epilogue: y = acc + D x. Accumulator quarter gq of column tile pt
+            // holds p = 32 pt + 8 gq + 4 hf + (0..3) of token j: read those four
+            // x values from the tile and add. For bf16, the two lane halves then
+            // swap halves of quarters 2g and 2g+1 (v_permlane32_swap), so that
+            // each lane holds 8 consecutive p (16 bytes) and a lane pair writes
+            // 32 contiguous bytes of row j; fp32 stores 16 bytes per quarter.
+            // the next head's vectors, before this head's stores: waiting for
+            // their loads then needs only the copies issued after them
+            if (more) store_vec(vn);
+            unsigned char* yh = ybase + (int64_t)hh * hs * P * ESZ;
+            const uint32_t ystride = (uint32_t)(H * P * ESZ);
+            const bool jok = jl < qch;
 #pragma unroll
-            for (int kt = 0; kt < 7; ++kt) {
-                if (kt < rt) {
-                    const float vj = fast_exp2(c2j - c2v[kt * 32 + 31]);
-                    V8 aop[2];
+            for (int pt = 0; pt < PT; ++pt) {
+                if constexpr (ESZ == 2) {
+#pragma unroll
+                    for (int gp = 0; gp < 2; ++gp) {
+                        uint32_t w[2][2];
+#pragma unroll
+                        for (int q = 0; q < 2; ++q) {
+                            const int gq = 2 * gp + q;
+                            const int xo = tile_byte<XRC>(jl, (pt * 32 + 8 * gq + 4 * hf) * ESZ);
+                            const bf16x4 xv = *reinterpret_cast<const bf16x4*>(xt + xo);
+                            bf16x4 yv;
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) yv[r] = from_f32<T>(acc[pt][4 * gq + r] + Dh * to_f32(xv[r]));
+                            const u32x2 wv = __builtin_bit_cast(u32x2, yv);
+                            w[q][0] = wv[0];
+                            w[q][1] = wv[1];
+                        }
+#pragma unroll
+                        for (int k = 0; k < 2; ++k) {
+                            const auto sw = __builtin_amdgcn_permlane32_swap(w[0][k], w[1][k], false, false);
+                            w[0][k] = sw[0];
+                            w[1][k] = sw[1];
+                        }
+                        const int p0 = pt * 32 + 8 * (2 * gp + hf);
+                        u32x4 out;
+                        out[0] = w[0][0]; out[1] = w[0][1]; out[2] = w[1][0]; out[3] = w[1][1];
+                        if (jok && p0 < (int)P)
+                            *(__attribute__((address_space(1))) u32x4*)(yh + (uint32_t)jl * ystride + p0 * ESZ) = out;
+                        else
+                            stored_all = false;
+                    }
+                } else {
 #pragma unroll
                     for (int gq = 0; gq < 4; ++gq) {
-                        const f32x4 u4 = *reinterpret_cast<const f32x4*>(uv + kt * 32 + 8 * gq + 4 * hf);
+                        const int p0 = pt * 32 + 8 * gq + 4 * hf;
+                        const int xo = tile_byte<XRC>(jl, p0 * ESZ);
+                        const f32x4 xv = *reinterpret_cast<const f32x4*>(xt + xo);
+                        f32x4 yv;
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int idx = 4 * gq + r;
-                            aop[idx >> 3][idx & 7] = from_f32<T>(to_f32(cb[kt][idx >> 3][idx & 7]) * vj * u4[r]);
-                        }
+                        for (int r = 0; r < 4; ++r) yv[r] = acc[pt][4 * gq + r] + Dh * xv[r];
+                        if (jok && p0 < (int)P)
+                            *(__attribute__((address_space(1))) f32x4*)(yh + (uint32_t)jl * ystride + p0 * ESZ) = yv;
+                        else
+                            stored_all = false;
                     }
-#pragma unroll
-                    for (int s = 0; s < 2; ++s)
-#pragma unroll
-                        for (int pt = 0; pt < PT; ++pt)
-                            mma_k16(acc[pt], aop[s], x_frag<T, XRC>(xt, 2 * kt + s, pt, xoa, xob, lane));
-                }
-            }
-            // the diagonal tile: direct decay; the causal mask (i <= j) enters as a
-            // -inf exponent for i > j, so exp2 gives exactly 0 with no lane masks
-            V8 xd[PT][2];
-            {
-                V8 aop[2];
-#pragma unroll
-                for (int gq = 0; gq < 4; ++gq) {
-                    const int ib = rt * 32 + 8 * gq + 4 * hf;
-                    const f32x4 ci = *reinterpret_cast<const f32x4*>(c2v + ib);
-                    const f32x4 di = *reinterpret_cast<const f32x4*>(dtv + ib);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int idx = 4 * gq + r;
-                        const float pen = __int_as_float(((jl - (ib + r)) >> 31) & (int)0xff800000u);
-                        const float m = to_f32(cbd[idx >> 3][idx & 7]) * fast_exp2((c2j - ci[r]) + pen) * di[r];
-                        aop[idx >> 3][idx & 7] = from_f32<T>(m);
-                    }
-                }
-#pragma unroll
-                for (int s = 0; s < 2; ++s)
-#pragma unroll
-                    for (int pt = 0; pt < PT; ++pt) {
-                        xd[pt][s] = x_frag<T, XRC>(xt, 2 * rt + s, pt, xoa, xob, lane);
-                        mma_k16(acc[pt], aop[s], xd[pt][s]);
-                    }
-            }
-
-            // epilogue: y = acc + D x_j, staged through this wave's LDS slab
-            // (8 rows at a time: accumulator quarter gq holds rows 8gq + 4hf + r)
-            // and written as 16-byte row segments
-            const float Dh = ldg(p.D + h0 + hh);
-            unsigned char* yh = ybase + (int64_t)hh * P * ESZ;
-            const uint32_t ystride = (uint32_t)(H * P * ESZ);
-            constexpr int RB = PT * 32 * ESZ;                   // staged row bytes
-#pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-#pragma unroll
-                for (int pt = 0; pt < PT; ++pt) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int e = 4 * (gq & 1) + r;
-                        *reinterpret_cast<T*>(yst + (4 * hf + r) * RB + (pt * 32 + l32) * ESZ) =
-                            from_f32<T>(acc[pt][4 * gq + r] + Dh * to_f32(xd[pt][gq >> 1][e]));
-                    }
-                }
-#pragma unroll
-                for (int k = 0; k < Cfg::NSTORE; ++k) {
-                    const int idx = k * 64 + lane;
-                    const int jr = idx / (RB / 16), cb16 = idx % (RB / 16);
-                    const u32x4 val = *reinterpret_cast<const u32x4*>(yst + (idx < Cfg::YCHUNKS ? idx : 0) * 16);
-                    const int j = rt * 32 + 8 * gq + jr;
-                    if (idx < Cfg::YCHUNKS && j < qch && cb16 * 16 < (int)(P * ESZ))
-                        *(__attribute__((address_space(1))) u32x4*)(yh + (uint32_t)j * ystride + cb16 * 16) = val;
-                    else if (idx < Cfg::YCHUNKS)
-                        stored_all = false;
                 }
             }
         }
-        if (more) store_vec(buf ^ 1);
+        if (more && !active) store_vec(vn);
+        return stored_all;
+    };
+
+    for (int hh = 0; hh < nh; ++hh) {
+        const int buf = hh & 1;
+        unsigned char* const xcur = smem + (NBX == 2 ? buf : 0) * XB;
+        unsigned char* const hcur = hb0 + (NBH == 2 ? buf : 0) * Cfg::HBYTES;
+        unsigned char* const xnext = smem + (NBX == 2 ? buf ^ 1 : 0) * XB;
+        unsigned char* const hnext = hb0 + (NBH == 2 ? buf ^ 1 : 0) * Cfg::HBYTES;
+        const bool stored_all = head(hh, xcur, hcur, vb0 + buf * (VB / 4), cbw, xnext, hnext, vb0 + (buf ^ 1) * (VB / 4),
+                                     __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dlane), hh)));
         // the next head's copies were issued before this head's stores: wait
         // for everything but the stores just issued (all lanes stored) or all
         if (__builtin_amdgcn_readfirstlane(__any(!stored_all) ? 1 : 0) == 0 && active)
-            wait_vmem_le<4 * Cfg::NSTORE>();
+            wait_vmem_le<(sizeof(T) == 2 ? 2 : 4) * PT>();   // this head's y stores
         else
             wait_vmem();
         __syncthreads();
-        if (more && (NBX == 1 || (NBH == 1 && c > 0))) {   // single-buffered tiles
-            if (NBX == 1) issue_x(hh + 1, 0);
-            if (NBH == 1 && c > 0) issue_h(hh + 1, 0);
+        if (hh + 1 < nh && (NBX == 1 || (NBH == 1 && c > 0))) {   // single-buffered tiles
+            if (NBX == 1) issue_x(hh + 1, xnext);
+            if (NBH == 1 && c > 0) issue_h(hh + 1, hnext);
             wait_vmem();
             __syncthreads();
         }
     }
 }
 
-template <typename T, int PT, int NT, typename ST, int NBX, int NBH>
+template <typename T, int PT, int NT, typename ST, int NBX, int NBH, bool CBL>
 static hipError_t launch_sc2(const Params& p, int hpw, int lds, hipStream_t s) {
-    auto kern = ssd_chunk_scan_kernel<T, PT, NT, ST, NBX, NBH>;
+    auto kern = ssd_chunk_scan_kernel<T, PT, NT, ST, NBX, NBH, CBL>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
@@ -397,9 +515,15 @@ static hipError_t launch_sc(const Params& p, hipStream_t s) {
     using Cfg = ScanCfg<T, PT, NT, ST>;
     const int Q = (int)p.chunk;
     const int hpw = scan_hpw(p);
-    if (Cfg::lds(Q, 2, 2) <= kScanMaxLds) return launch_sc2<T, PT, NT, ST, 2, 2>(p, hpw, Cfg::lds(Q, 2, 2), s);
-    if (Cfg::lds(Q, 2, 1) <= kScanMaxLds) return launch_sc2<T, PT, NT, ST, 2, 1>(p, hpw, Cfg::lds(Q, 2, 1), s);
-    if (Cfg::lds(Q, 1, 1) <= kScanMaxLds) return launch_sc2<T, PT, NT, ST, 1, 1>(p, hpw, Cfg::lds(Q, 1, 1), s);
+    // prefer C B^T in LDS (frees the registers that would hold it), then
+    // double-buffered copies
+#define SSD_SC_TRY(NBX_, NBH_, CBL_)                                                           \
+    if (Cfg::lds(Q, NBX_, NBH_, CBL_) <= kScanMaxLds)                                          \
+        return launch_sc2<T, PT, NT, ST, NBX_, NBH_, CBL_>(p, hpw, Cfg::lds(Q, NBX_, NBH_, CBL_), s);
+    if constexpr (sizeof(T) == 2 && sizeof(ST) == 2) { SSD_SC_TRY(2, 2, true) }
+    if constexpr (sizeof(T) == 2) { SSD_SC_TRY(2, 1, true) }
+    SSD_SC_TRY(1, 1, true) SSD_SC_TRY(1, 1, false)
+#undef SSD_SC_TRY
     return hipErrorInvalidValue;
 }
 
@@ -426,7 +550,7 @@ hipError_t launch_chunk_scan(const Params& p, int dtype, int state_dtype, hipStr
 int chunk_scan_lds_bytes(int dtype, int state_dtype, int64_t P, int64_t N, int64_t Q) {
     const int esz = dtype == 1 ? 2 : 4, ssz = state_dtype == 1 ? 2 : 4;
     const int pp = (int)((P + 31) / 32) * 32, np = (int)((N + 31) / 32) * 32;
-    return (int)Q * pp * esz + pp * np * ssz + 2 * 4 * (int)Q * 4 + kScanWaves * 8 * pp * esz;
+    return (int)Q * pp * esz + pp * np * ssz + 2 * 4 * (int)Q * 4;
 }
 
 }  // namespace ssd

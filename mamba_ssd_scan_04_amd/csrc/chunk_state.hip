@@ -68,12 +68,10 @@ __device__ __forceinline__ void dma_plan(int (&off)[NI], int valid_chunks, uint3
 template <int NI>
 __device__ __forceinline__ void dma_issue(unsigned char* lds, const unsigned char* gbase, const int (&off)[NI],
                                           int wave) {
+    const __amdgpu_buffer_rsrc_t rs = raw_rsrc(gbase);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-        if (off[i] >= 0)
-            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(gbase + off[i]),
-                                             (__attribute__((address_space(3))) void*)(lds + (wave + 4 * i) * 1024),
-                                             16, 0, 0);
+        if (off[i] >= 0) dma16(rs, (uint32_t)off[i], lds + (wave + 4 * i) * 1024);
     }
 }
 
@@ -128,8 +126,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     int offb[Cfg::NDB], offx[Cfg::NDX];
     dma_plan<Cfg::BRC, Cfg::NDB>(offb, bvalid, bstride, wave, lane);
     dma_plan<Cfg::XRC, Cfg::NDX>(offx, xvalid, xstride, wave, lane);
-    auto issue = [&](int blk, int buf) {
-        unsigned char* base = smem + buf * Cfg::BUF;
+    auto issue = [&](int blk, unsigned char* base) {
         const int r0 = blk * kStateKB;
         if (r0 + kStateKB <= qc) {          // full block: precomputed lane offsets
             dma_issue<Cfg::NDB>(base, bbase + (uint32_t)r0 * bstride, offb, wave);
@@ -176,16 +173,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
     const int nblk = Q / kStateKB;
     constexpr int AHEAD = NBUF - 1;     // blocks in flight beyond the one in use
-    for (int k = 0; k < AHEAD && k < nblk; ++k) issue(k, k);
+    for (int k = 0; k < AHEAD && k < nblk; ++k) issue(k, smem + k * Cfg::BUF);
     wait_vmem_le_rt(nblk > 1 && AHEAD > 1 ? per_block : 0);   // block 0 landed
     __syncthreads();
-    for (int blk = 0; blk < nblk; ++blk) {
-        const int buf = blk % NBUF;
-        if (blk + AHEAD < nblk) issue(blk + AHEAD, (blk + AHEAD) % NBUF);
+
+    // One block: start the copy of block blk + AHEAD into `next`, then run the
+    // matrix cores on block blk in `base`. The three LDS regions are passed as
+    // non-aliasing pointers so that the compiler knows the reads of `base` and
+    // `wrow` do not depend on the copy in flight into `next` and does not wait
+    // for it (the copy is waited for explicitly, one block later).
+    auto step = [&](int blk, const unsigned char* __restrict__ base, unsigned char* __restrict__ next,
+                    const float* __restrict__ wrow) __attribute__((always_inline)) {
+        if (blk + AHEAD < nblk) issue(blk + AHEAD, next);
         if (active) {
-            const unsigned char* base = smem + buf * Cfg::BUF;
             const unsigned char* xtile = base + Cfg::BBYTES + hh * Cfg::XBYTES;
-            const float* wrow = wv + hh * Q + blk * kStateKB;
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
                 const int rofs_x = 16 * s * Cfg::XRC * 16, rofs_b = 16 * s * Cfg::BRC * 16;
@@ -222,6 +223,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                     for (int n = 0; n < NT; ++n) mma_k16(acc[i][n], bf[n], xf[i]);
             }
         }
+    };
+    for (int blk = 0; blk < nblk; ++blk) {
+        step(blk, smem + (blk % NBUF) * Cfg::BUF, smem + ((blk + AHEAD) % NBUF) * Cfg::BUF,
+             wv + hh * Q + blk * kStateKB);
         // block blk+1 must have landed; later blocks may still be in flight
         const int later = min(AHEAD - 1, nblk - 2 - blk);
         wait_vmem_le_rt(later > 0 ? later * per_block : 0);

@@ -13,6 +13,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace ssd {
 
 typedef __bf16 bf16;
@@ -22,6 +24,7 @@ typedef __attribute__((ext_vector_type(8))) float f32x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -144,18 +147,33 @@ __device__ __forceinline__ int tile_byte(int r, int b) {
     return r * RC * 16 + (((b >> 4) ^ swz<RC>(r)) << 4) + (b & 15);
 }
 
+// Buffer resource (V#) for raw byte-addressed loads from a wave-uniform base:
+// no stride, 32-bit data format, offsets up to 2^31 - 1.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7FFFFFFF, 0x00020000);
+}
+
+// One 16-byte global -> LDS copy per lane, straight into LDS (no registers):
+// lane l writes LDS bytes [lds + 16 l, lds + 16 l + 16) from rs + voff. The
+// buffer form (not the global one) lets the compiler keep exact counts of
+// the LDS reads in flight around it.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, unsigned char* lds) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+}
+
 // Asynchronous global -> LDS copy of a rows x RC-chunk tile. Every lane of a
-// wavefront copies one 16-byte chunk per instruction straight into LDS (no
-// registers); instruction k of the tile writes LDS bytes [1024 k, 1024 k + 1024).
-// The source of physical chunk (r, pc) is logical chunk c = pc ^ swz(r) of
-// row r: gbase + r * row_stride + 16 c, with r clamped to valid_rows - 1 and c
-// to valid_chunks - 1 (rows or columns past the data are filled with copies of
-// real data: the kernels only ever give them zero weight or leave their
-// outputs unstored). gbase is uniform; offsets are 32-bit.
+// wavefront copies one 16-byte chunk per instruction; instruction k of the
+// tile writes LDS bytes [1024 k, 1024 k + 1024). The source of physical chunk
+// (r, pc) is logical chunk c = pc ^ swz(r) of row r: gbase + r * row_stride +
+// 16 c, with r clamped to valid_rows - 1 and c to valid_chunks - 1 (rows or
+// columns past the data are filled with copies of real data: the kernels only
+// ever give them zero weight or leave their outputs unstored). gbase is
+// uniform; offsets are 32-bit.
 template <int RC>
 __device__ __forceinline__ void dma_tile(unsigned char* lds, int rows, int valid_rows, int valid_chunks,
                                          const unsigned char* gbase, uint32_t row_stride, int wave,
                                          int nwaves, int lane) {
+    const __amdgpu_buffer_rsrc_t rs = raw_rsrc(gbase);
     const int total = rows * RC;   // a multiple of 64
     for (int k = wave; k * 64 < total; k += nwaves) {
         const int P = k * 64 + lane;
@@ -163,10 +181,38 @@ __device__ __forceinline__ void dma_tile(unsigned char* lds, int rows, int valid
         int c = (P % RC) ^ swz<RC>(r);
         c = c < valid_chunks ? c : valid_chunks - 1;
         const int rr = r < valid_rows ? r : valid_rows - 1;
-        const unsigned char* src = gbase + ((uint32_t)rr * row_stride + 16u * (uint32_t)c);
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                         (__attribute__((address_space(3))) void*)(lds + k * 1024), 16, 0, 0);
+        dma16(rs, (uint32_t)rr * row_stride + 16u * (uint32_t)c, lds + k * 1024);
     }
+}
+
+// The same copies as dma_tile, planned once: lane offsets of the at most NI
+// instructions a wavefront issues (instruction i is tile instruction
+// wave + nwaves * i; -1 = none), then issued for any source base.
+template <int RC, int NI>
+__device__ __forceinline__ void dma_tile_plan(int (&off)[NI], int rows, int valid_rows, int valid_chunks,
+                                              uint32_t row_stride, int wave, int nwaves, int lane) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int k = wave + nwaves * i;
+        if (k * 64 < rows * RC) {
+            const int P = k * 64 + lane;
+            const int r = P / RC;
+            int c = (P % RC) ^ swz<RC>(r);
+            c = c < valid_chunks ? c : valid_chunks - 1;
+            const int rr = r < valid_rows ? r : valid_rows - 1;
+            off[i] = (int)((uint32_t)rr * row_stride + 16u * (uint32_t)c);
+        } else {
+            off[i] = -1;
+        }
+    }
+}
+template <int NI>
+__device__ __forceinline__ void dma_tile_issue(unsigned char* lds, const unsigned char* gbase, const int (&off)[NI],
+                                               int wave, int nwaves) {
+    const __amdgpu_buffer_rsrc_t rs = raw_rsrc(gbase);
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+        if (off[i] >= 0) dma16(rs, (uint32_t)off[i], lds + (wave + nwaves * i) * 1024);
 }
 
 // Loads through explicit global-address-space pointers (not flat).
@@ -317,4 +363,22 @@ __device__ __forceinline__ int xcd_logical_block() {
 // 2^x on the hardware transcendental unit (v_exp_f32): results below the
 // smallest normal flush to 0, 2^-inf = 0.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Value of lane n of this lane's 16-lane row (DPP row_newbcast); folded by
+// the compiler into the consuming VALU instruction as a DPP source operand.
+template <int N>
+__device__ __forceinline__ float row_bcast(float v) {
+    static_assert(N >= 0 && N < 16, "row lane");
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + N, 0xF, 0xF, false));
+}
+
+// f(std::integral_constant<int, I>) for I = 0 .. N-1, unrolled at compile time.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 }  // namespace ssd

@@ -74,7 +74,8 @@ def dims(**kw):
     (dict(dtype="fp32", headdim=128, dstate=256, chunk_size=256), UNSUP),  # fp32 tile > LDS
     (dict(headdim=128, dstate=256, chunk_size=256), UNSUP),  # x + fp32 state tiles > LDS
     (dict(headdim=128, dstate=256, chunk_size=256, state_dtype="bf16"), OK),
-    (dict(headdim=128, dstate=256, chunk_size=64), UNSUP),   # fp32 state tile alone is 128 KB
+    (dict(headdim=128, dstate=256, chunk_size=64), OK),      # 16 KB x + 128 KB fp32 state tile + vectors
+    (dict(headdim=128, dstate=256, chunk_size=128), UNSUP),  # 32 KB x + 128 KB state tile
     (dict(headdim=128, dstate=256, chunk_size=64, state_dtype="bf16"), OK),
     (dict(headdim=64, dstate=256, chunk_size=256), OK),
 ])

@@ -69,6 +69,14 @@ def test_group_patterns(H, G):
     check(w, inputs.generate_slow_decay(w, seed=5))
 
 
+@pytest.mark.parametrize("P,N,state,Q", [(128, 256, "fp32", 64), (128, 256, "bf16", 128), (64, 256, "fp32", 256)])
+def test_large_state_tiles(P, N, state, Q):
+    """Head and state sizes whose LDS tiles leave little room: the chunk scan
+    falls back to single buffers and, at the largest, to C B^T in registers."""
+    w = workload("m125", batch=1, seqlen=2 * Q + 40, nheads=3, headdim=P, dstate=N, chunk_size=Q)
+    check(w, inputs.generate_slow_decay(w, seed=12), state)
+
+
 @pytest.mark.parametrize("P,N,Q", [(16, 16, 64), (64, 128, 128), (32, 32, 32), (64, 64, 256)])
 def test_fp32_inputs(P, N, Q):
     w = workload("tiny", batch=2, seqlen=333, nheads=3, headdim=P, dstate=N, chunk_size=Q)
