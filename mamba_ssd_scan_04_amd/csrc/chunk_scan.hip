@@ -167,14 +167,22 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
     // D of this workgroup's heads, lane l holding head h0 + l nhb (read per head
     // with a lane broadcast, so no scalar loads sit in the head loop)
     const float dlane = ldg(p.D + h0 + (lane < nh ? lane : 0) * hs);
-    // head 0's tiles start moving before phase A
-    if (nh > 0) {
+    // ---- phase A: this wave's C rows and C B^T row of tiles, once per workgroup ----
+    // B is staged through LDS in slices of whole 32-token key tiles, in the
+    // x buffer that head 0 does not use (or in head 0's, whose copy then
+    // starts after phase A); if not even one key tile fits there, B tiles are
+    // read from global memory instead.
+    constexpr int BRC = NT * 32 * ESZ / 16;                    // 16-byte chunks per B row
+    constexpr int BTILE = 32 * BRC * 16;                       // one 32-token B tile
+    unsigned char* const stg = smem + (NBX == 2 ? XB : 0);
+    const int tps = XB / BTILE;                                // B tiles per slice
+    const bool bstage = tps > 0;
+    if (nh > 0) {   // head 0's tiles start moving before phase A
         load_vec(0);
-        issue_x(0, smem);
+        if (NBX == 2 || !bstage) issue_x(0, smem);
         if (c > 0) issue_h(0, hb0);
     }
 
-    // ---- phase A: this wave's C rows and C B^T row of tiles, once per workgroup ----
     const int nlast = (int)N - 8;
     V8 creg[KS];
     V8 cb[CBL ? 1 : 7][2];   // key tiles kt < rt, in registers unless kept in LDS
@@ -182,16 +190,71 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
     // this row tile's off-diagonal tiles in LDS: tile kt at cbw + kt * CBTILE,
     // lane l's 8 low / 8 high elements at l * 8 and (64 + l) * 8 elements
     unsigned char* const cbw = cbl0 + (rt > 0 ? rt * (rt - 1) / 2 : 0) * Cfg::CBTILE;
+    auto off = [&](int row, int ks) {
+        return (uint32_t)min(row, qc - 1) * bcs + (uint32_t)min(ks * 16 + hf * 8, nlast);
+    };
     if (active) {
-        auto off = [&](int row, int ks) {
-            return (uint32_t)min(row, qc - 1) * bcs + (uint32_t)min(ks * 16 + hf * 8, nlast);
-        };
         const int jl = rt * 32 + l32;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const V8 raw = ldg8(cbase + off(jl, ks));
             creg[ks] = (jl < qc && ks * 16 + hf * 8 < (int)N) ? raw : zero8<T>();
         }
+    }
+    // round tile kt of C B^T to the operand type and keep it
+    auto keep_tile = [&](int kt, const f32x16& acc) {
+        V8 lo, hi;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            lo[e] = from_f32<T>(acc[e]);
+            hi[e] = from_f32<T>(acc[8 + e]);
+        }
+        if (kt < rt) {
+            if constexpr (CBL) {
+                store8(reinterpret_cast<T*>(cbw + kt * Cfg::CBTILE) + lane * 8, lo);
+                store8(reinterpret_cast<T*>(cbw + kt * Cfg::CBTILE) + (64 + lane) * 8, hi);
+            } else {
+                cb[kt < 7 ? kt : 6][0] = lo;
+                cb[kt < 7 ? kt : 6][1] = hi;
+            }
+        } else {
+            cbd[0] = lo;
+            cbd[1] = hi;
+        }
+    };
+    if (bstage) {
+        const unsigned char* bbytes = reinterpret_cast<const unsigned char*>(bbase);
+        const uint32_t bstride = (uint32_t)(G * N * ESZ);
+        const int bvalid = (int)(N * ESZ / 16);
+        for (int s0 = 0; s0 < RT; s0 += tps) {
+            const int s1 = min(s0 + tps, RT);
+            if (s0 > 0) __syncthreads();   // the previous slice has been read
+            // rows past the chunk's last token re-read that token (their
+            // products get zero weight); a slice wholly past it reads only it
+            const int rb = min(s0 * 32, qc - 1);
+            dma_tile<BRC>(stg, (s1 - s0) * 32, qc - rb, bvalid, bbytes + (size_t)rb * bstride, bstride, wave,
+                          kScanWaves, lane);
+            wait_vmem();
+            __syncthreads();
+            if (active) {
+                for (int kt = s0; kt < s1 && kt <= rt; ++kt) {
+                    const int row = (kt - s0) * 32 + l32;
+                    f32x16 acc = zero16();
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) {
+                        V8 a = row8<BRC>(reinterpret_cast<const T*>(stg), row, ks * 16 + hf * 8);
+                        if (ks * 16 + hf * 8 >= (int)N) a = zero8<T>();
+                        mma_k16(acc, a, creg[ks]);
+                    }
+                    keep_tile(kt, acc);
+                }
+            }
+        }
+        if (NBX == 1 && nh > 0) {   // head 0's x goes where B was staged
+            __syncthreads();
+            issue_x(0, smem);
+        }
+    } else if (active) {
         V8 bnext[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) bnext[ks] = ldg8(bbase + off(l32, ks));
@@ -209,24 +272,7 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
                 f32x16 acc = zero16();
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) mma_k16(acc, bcur[ks], creg[ks]);
-                V8 lo, hi;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    lo[e] = from_f32<T>(acc[e]);
-                    hi[e] = from_f32<T>(acc[8 + e]);
-                }
-                if (kt < rt) {
-                    if constexpr (CBL) {
-                        store8(reinterpret_cast<T*>(cbw + kt * Cfg::CBTILE) + lane * 8, lo);
-                        store8(reinterpret_cast<T*>(cbw + kt * Cfg::CBTILE) + (64 + lane) * 8, hi);
-                    } else {
-                        cb[kt < 7 ? kt : 6][0] = lo;
-                        cb[kt < 7 ? kt : 6][1] = hi;
-                    }
-                } else {
-                    cbd[0] = lo;
-                    cbd[1] = hi;
-                }
+                keep_tile(kt, acc);
             }
         }
     }
