@@ -100,7 +100,9 @@ ssd_status ssd_stage_sizes(const ssd_dims* d, size_t* cs_bytes, size_t* states_b
  * Full forward: Knowl 2's inputs X, A, B, C and chunk size Q, its outputs Y and
  * h_final ("Input"/"Output" lines of the algorithm), with the per-head
  * discretisation dt, A and the skip term D. Enqueues, in order,
- * ssd_chunk_cumsum, ssd_chunk_state, ssd_state_passing and ssd_chunk_scan.
+ * ssd_chunk_cumsum_state (stages 1 and 2 in one launch), ssd_state_passing
+ * and ssd_chunk_scan; the result is bitwise that of the four stage entry
+ * points run one after another.
  *   x [b,T,H,P], dt [b,T,H], A [H], B [b,T,G,N], C [b,T,G,N], D [H]: inputs
  *   y [b,T,H,P] (out, dtype), final_state [b,H,N,P] (out, fp32)
  *   workspace: device buffer of at least ssd_workspace_size(d) bytes; its
@@ -130,6 +132,15 @@ ssd_status ssd_chunk_cumsum(const ssd_dims* d, const float* dt, const float* A, 
  */
 ssd_status ssd_chunk_state(const ssd_dims* d, const void* x, const float* dt, const void* B,
                            const float* cs, void* states, hipStream_t stream);
+
+/*
+ * Stages 1 and 2 in one launch: each chunk-state workgroup first forms the
+ * in-chunk prefix sums of its heads (the arithmetic of ssd_chunk_cumsum,
+ * bitwise the same), writes them to cs and uses them for the chunk states.
+ *   x, dt, A, B in; cs [b,H,nc,Q] fp32 out; states [b,nc,H,P,N] out.
+ */
+ssd_status ssd_chunk_cumsum_state(const ssd_dims* d, const void* x, const float* dt, const float* A,
+                                  const void* B, float* cs, void* states, hipStream_t stream);
 
 /*
  * Stage 3 (Knowl 2, the sequential loop over chunks h_{c+1} = (prod a) h_c + S_c,

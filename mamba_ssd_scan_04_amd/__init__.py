@@ -66,6 +66,8 @@ def load_library() -> ctypes.CDLL:
     lib.ssd_forward.restype = st
     lib.ssd_chunk_cumsum.argtypes, lib.ssd_chunk_cumsum.restype = [P, vp, vp, vp, vp], st
     lib.ssd_chunk_state.argtypes, lib.ssd_chunk_state.restype = [P, vp, vp, vp, vp, vp, vp], st
+    lib.ssd_chunk_cumsum_state.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
+    lib.ssd_chunk_cumsum_state.restype = st
     lib.ssd_state_passing.argtypes, lib.ssd_state_passing.restype = [P, vp, vp, vp, vp], st
     lib.ssd_chunk_scan.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.ssd_chunk_scan.restype = st
@@ -155,6 +157,12 @@ def ssd_chunk_state(d, x, dt, B, cs, states, stream=None):
     s = _stream(x.device) if stream is None else stream
     _check(load_library().ssd_chunk_state(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(B), _ptr(cs),
                                           _ptr(states), s))
+
+
+def ssd_chunk_cumsum_state(d, x, dt, A, B, cs, states, stream=None):
+    s = _stream(x.device) if stream is None else stream
+    _check(load_library().ssd_chunk_cumsum_state(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
+                                                 _ptr(cs), _ptr(states), s))
 
 
 def ssd_state_passing(d, cs, states, final_state, stream=None):

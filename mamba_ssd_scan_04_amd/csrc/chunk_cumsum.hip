@@ -46,28 +46,9 @@ __global__ __launch_bounds__(256) void ssd_chunk_cumsum_kernel(Params p) {
     const int active = Q / per;              // lanes holding tokens
     for (int hh = wave; hh < nh; hh += 4) {
         float v[4];
-        float run = 0.0f;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            if (k < per && lane < active) run += tile[lane * per + k][hh];
-            v[k] = run;
-        }
-        const float incl = wave_inclusive_scan(run, lane);
-        const float base = incl - run;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) v[k] += base;
-        if (qc < Q) {
-            // padding positions take the exact value of the last real token
-            const int src = (qc - 1) / per, ks = (qc - 1) % per;
-            float mine = v[0];
-#pragma unroll
-            for (int k = 1; k < 4; ++k)
-                if (k == ks) mine = v[k];
-            const float lastv = __shfl(mine, src, 64);
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-                if (lane * per + k >= qc) v[k] = lastv;
-        }
+        for (int k = 0; k < 4; ++k) v[k] = (k < per && lane < active) ? tile[lane * per + k][hh] : 0.0f;
+        chunk_prefix(v, per, active, qc, lane);
         float* out = p.cs + ((b * H + h0 + hh) * p.nchunks + c) * Q;
         if (lane < active) {
             if (per == 4) {

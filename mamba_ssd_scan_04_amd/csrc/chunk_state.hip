@@ -109,14 +109,54 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // decay-to-chunk-end weights w_j for every head of the block
     const float* csbase = p.cs + ((b * H + h0) * nc + c) * Q;
     const float* dtbase = p.dt + tok0 * H + h0;
-    for (int idx = threadIdx.x; idx < HPW * Q; idx += blockDim.x) {
-        const int hq = idx / Q, j = idx % Q;
-        float wj = 0.0f;
-        if (hq < nh && j < qc) {
-            const float* csr = csbase + (int64_t)hq * nc * Q;
-            wj = exp2f((ldg(csr + Q - 1) - ldg(csr + j)) * kLog2e) * ldg(dtbase + hq + (uint32_t)j * (uint32_t)H);
+    if (p.fuse_cs) {
+        // the in-chunk cumulative decay of head hq = wave (the step of
+        // ssd_chunk_cumsum, same arithmetic), written out for the later
+        // kernels and used here directly
+        const int per = Q >= 64 ? Q / 64 : 1, nact = Q / per;
+        if (wave < HPW) {
+            const int hq = wave;
+            float dtv[4], v[4];
+            const float Ah = hq < nh ? ldg(p.A + h0 + hq) : 0.0f;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int j = lane * per + k;
+                dtv[k] = (hq < nh && k < per && lane < nact && j < qc) ? ldg(dtbase + hq + (uint32_t)j * (uint32_t)H) : 0.0f;
+                {
+#pragma clang fp contract(off)
+                    v[k] = dtv[k] * Ah;   // a rounded product, as ssd_chunk_cumsum forms it
+                }
+            }
+            chunk_prefix(v, per, nact, qc, lane);
+            const float last = __shfl(v[per - 1], nact - 1, 64);
+            if (hq < nh && lane < nact) {
+                float* out = p.cs + ((b * H + h0 + hq) * nc + c) * Q + lane * per;
+                if (per == 4) {
+                    f32x4 o;
+                    o[0] = v[0]; o[1] = v[1]; o[2] = v[2]; o[3] = v[3];
+                    *reinterpret_cast<f32x4*>(out) = o;
+                } else {
+                    for (int k = 0; k < per; ++k) out[k] = v[k];
+                }
+            }
+            if (lane < nact) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int j = lane * per + k;
+                    if (k < per) wv[hq * Q + j] = (hq < nh && j < qc) ? exp2f((last - v[k]) * kLog2e) * dtv[k] : 0.0f;
+                }
+            }
         }
-        wv[hq * Q + j] = wj;
+    } else {
+        for (int idx = threadIdx.x; idx < HPW * Q; idx += blockDim.x) {
+            const int hq = idx / Q, j = idx % Q;
+            float wj = 0.0f;
+            if (hq < nh && j < qc) {
+                const float* csr = csbase + (int64_t)hq * nc * Q;
+                wj = exp2f((ldg(csr + Q - 1) - ldg(csr + j)) * kLog2e) * ldg(dtbase + hq + (uint32_t)j * (uint32_t)H);
+            }
+            wv[hq * Q + j] = wj;
+        }
     }
 
     const unsigned char* bbase = static_cast<const unsigned char*>(p.B) + (tok0 * G + g) * N * ESZ;

@@ -140,6 +140,25 @@ ssd_status ssd_chunk_state(const ssd_dims* d, const void* x, const float* dt, co
     return to_status(ssd::launch_chunk_state(p, d->dtype, d->state_dtype, stream));
 }
 
+ssd_status ssd_chunk_cumsum_state(const ssd_dims* d, const void* x, const float* dt, const float* A,
+                                  const void* B, float* cs, void* states, hipStream_t stream) {
+    ssd_status st = ssd_check_dims(d);
+    if (st != SSD_OK) return st;
+    if (empty(d)) return SSD_OK;
+    if (!x || !dt || !A || !B || !cs || !states) return SSD_ERR_NULL_POINTER;
+    if (!aligned16(x) || !aligned16(dt) || !aligned16(A) || !aligned16(B) || !aligned16(cs) || !aligned16(states))
+        return SSD_ERR_MISALIGNED;
+    ssd::Params p = make_params(d);
+    p.x = x;
+    p.dt = dt;
+    p.A = A;
+    p.B = B;
+    p.cs = cs;
+    p.states = states;
+    p.fuse_cs = 1;
+    return to_status(ssd::launch_chunk_state(p, d->dtype, d->state_dtype, stream));
+}
+
 ssd_status ssd_state_passing(const ssd_dims* d, const float* cs, void* states, float* final_state,
                              hipStream_t stream) {
     ssd_status st = ssd_check_dims(d);
@@ -198,8 +217,7 @@ ssd_status ssd_forward(const ssd_dims* d, const void* x, const float* dt, const 
     if (workspace_bytes < ssd_workspace_size(d)) return SSD_ERR_WORKSPACE_TOO_SMALL;
     float* cs = static_cast<float*>(workspace);
     void* states = static_cast<unsigned char*>(workspace) + round_up(cs_bytes_of(d));
-    st = ssd_chunk_cumsum(d, dt, A, cs, stream);
-    if (st == SSD_OK) st = ssd_chunk_state(d, x, dt, B, cs, states, stream);
+    st = ssd_chunk_cumsum_state(d, x, dt, A, B, cs, states, stream);
     if (st == SSD_OK) st = ssd_state_passing(d, cs, states, final_state, stream);
     if (st == SSD_OK) st = ssd_chunk_scan(d, x, dt, B, C, D, cs, states, y, stream);
     return st;

@@ -39,6 +39,7 @@ struct Params {
     const float* D;
     float* cs;
     void* states;
+    int fuse_cs;        // chunk_state also computes (and writes) cs from dt and A
     void* y;
     float* final_state;
 };
@@ -110,6 +111,37 @@ __device__ __forceinline__ float wave_inclusive_scan(float v, int lane) {
         if (lane >= off) v += n;
     }
     return v;
+}
+
+// In-chunk inclusive prefix sum over one wavefront (the parallel scan of
+// "Transformers are SSMs", appendix B.2.2): lane l holds the `per` consecutive
+// values l*per .. l*per+per-1 in v[0..per) (per <= 4, lanes >= active hold
+// nothing); each lane sums its values serially, a wavefront scan of the lane
+// totals gives the offsets. Positions at or past qc then take the exact value
+// at qc - 1, so a short last chunk repeats its final value.
+__device__ __forceinline__ void chunk_prefix(float (&v)[4], int per, int active, int qc, int lane) {
+    float run = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        if (k < per && lane < active) run += v[k];
+        v[k] = run;
+    }
+    const float incl = wave_inclusive_scan(run, lane);
+    const float base = incl - run;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] += base;
+    const int qa = qc < per * active ? qc : per * active;
+    if (qa < per * active) {
+        const int src = (qa - 1) / per, ks = (qa - 1) % per;
+        float mine = v[0];
+#pragma unroll
+        for (int k = 1; k < 4; ++k)
+            if (k == ks) mine = v[k];
+        const float lastv = __shfl(mine, src, 64);
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (lane * per + k >= qa) v[k] = lastv;
+    }
 }
 
 // Position of token i_local (0..15) of a 16-token group in the "fragment

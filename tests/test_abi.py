@@ -138,6 +138,8 @@ def test_stage_argument_errors(lib):
     assert lib.ssd_chunk_cumsum(P(d), None, a, a, None) == NULLP
     assert lib.ssd_chunk_cumsum(P(d), a, a, _fake(0x200002), None) == MISAL
     assert lib.ssd_chunk_state(P(d), a, a, a, a, None, None) == NULLP
+    assert lib.ssd_chunk_cumsum_state(P(d), a, a, None, a, a, a, None) == NULLP
+    assert lib.ssd_chunk_cumsum_state(P(d), a, a, a, a, _fake(0x200004), a, None) == MISAL
     assert lib.ssd_state_passing(P(d), a, a, None, None) == NULLP
     assert lib.ssd_chunk_scan(P(d), a, a, a, a, a, a, a, None, None) == NULLP
     assert lib.ssd_chunk_scan(P(dims(headdim=40)), a, a, a, a, a, a, a, a, None) == UNSUP
@@ -145,6 +147,7 @@ def test_stage_argument_errors(lib):
     e = dims(seqlen=0)
     assert lib.ssd_chunk_cumsum(P(e), None, None, None, None) == OK
     assert lib.ssd_chunk_state(P(e), None, None, None, None, None, None) == OK
+    assert lib.ssd_chunk_cumsum_state(P(e), None, None, None, None, None, None, None) == OK
     assert lib.ssd_chunk_scan(P(e), None, None, None, None, None, None, None, None, None) == OK
 
 

@@ -169,3 +169,22 @@ def test_stage_parity(state_dtype):
     assert oracle.rel_err(h_in, snaps) < tol
     assert oracle.rel_err(out["final"].cpu().numpy(), fin_ref) < tol
     assert oracle.rel_err(out["y"].float().cpu().numpy(), y_ref) < tol
+
+
+@pytest.mark.parametrize("T", [1000, 512])
+def test_forward_matches_stage_entry_points(T):
+    """ssd_forward fuses the in-chunk cumulative decay into its chunk-state
+    launch; the result must be bitwise that of the four stage entry points."""
+    w = workload("m125", batch=2, seqlen=T, nheads=6, ngroups=2)
+    dev = to_dev(inputs.generate_slow_decay(w, seed=13))
+    say(f"fused-vs-stages case {w.describe()}")
+    for st in ("fp32", "bf16"):
+        y, fin = ssd.forward(dev["x"], dev["dt"], dev["A"], dev["B"], dev["C"], dev["D"], w.chunk_size, st)
+        out = ssd.stages(dev["x"], dev["dt"], dev["A"], dev["B"], dev["C"], dev["D"], w.chunk_size, st)
+        d = ssd.dims_of(dev["x"], dev["B"], w.chunk_size, st)
+        cs = torch.full_like(out["cs"], float("nan"))
+        S = torch.full_like(out["S"], float("nan"))
+        ssd.ssd_chunk_cumsum_state(d, dev["x"], dev["dt"], dev["A"], dev["B"], cs, S)
+        torch.cuda.synchronize()
+        assert torch.equal(y, out["y"]) and torch.equal(fin, out["final"])
+        assert torch.equal(cs, out["cs"]) and torch.equal(S, out["S"])
