@@ -228,14 +228,14 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
         const int bvalid = (int)(N * ESZ / 16);
         for (int s0 = 0; s0 < RT; s0 += tps) {
             const int s1 = min(s0 + tps, RT);
-            if (s0 > 0) __syncthreads();   // the previous slice has been read
+            if (s0 > 0) lds_barrier();   // the previous slice has been read
             // rows past the chunk's last token re-read that token (their
             // products get zero weight); a slice wholly past it reads only it
             const int rb = min(s0 * 32, qc - 1);
             dma_tile<BRC>(stg, (s1 - s0) * 32, qc - rb, bvalid, bbytes + (size_t)rb * bstride, bstride, wave,
                           kScanWaves, lane);
             wait_vmem();
-            __syncthreads();
+            lds_barrier();
             if (active) {
                 for (int kt = s0; kt < s1 && kt <= rt; ++kt) {
                     const int row = (kt - s0) * 32 + l32;
@@ -251,7 +251,7 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
             }
         }
         if (NBX == 1 && nh > 0) {   // head 0's x goes where B was staged
-            __syncthreads();
+            lds_barrier();
             issue_x(0, smem);
         }
     } else if (active) {
@@ -290,7 +290,7 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
 
     if (nh > 0) store_vec(vb0);
     wait_vmem();
-    __syncthreads();
+    lds_barrier();
 
     // ---- phase B: heads ----
     // One head: start the copies of the next head's tiles into xn / hn (when
@@ -523,12 +523,12 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
             wait_vmem_le<(sizeof(T) == 2 ? 2 : 4) * PT>();   // this head's y stores
         else
             wait_vmem();
-        __syncthreads();
+        lds_barrier();
         if (hh + 1 < nh && (NBX == 1 || (NBH == 1 && c > 0))) {   // single-buffered tiles
             if (NBX == 1) issue_x(hh + 1, xnext);
             if (NBH == 1 && c > 0) issue_h(hh + 1, hnext);
             wait_vmem();
-            __syncthreads();
+            lds_barrier();
         }
     }
 }

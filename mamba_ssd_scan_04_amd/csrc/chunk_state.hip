@@ -215,7 +215,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     constexpr int AHEAD = NBUF - 1;     // blocks in flight beyond the one in use
     for (int k = 0; k < AHEAD && k < nblk; ++k) issue(k, smem + k * Cfg::BUF);
     wait_vmem_le_rt(nblk > 1 && AHEAD > 1 ? per_block : 0);   // block 0 landed
-    __syncthreads();
+    lds_barrier();
 
     // One block: start the copy of block blk + AHEAD into `next`, then run the
     // matrix cores on block blk in `base`. The three LDS regions are passed as
@@ -270,7 +270,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // block blk+1 must have landed; later blocks may still be in flight
         const int later = min(AHEAD - 1, nblk - 2 - blk);
         wait_vmem_le_rt(later > 0 ? later * per_block : 0);
-        __syncthreads();
+        lds_barrier();
     }
 
     if (active) {

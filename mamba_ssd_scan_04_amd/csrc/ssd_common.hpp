@@ -365,6 +365,21 @@ __device__ __forceinline__ void wait_vmem_le() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
+// Workgroup barrier for pipelines of global -> LDS copies. __syncthreads()
+// makes this wavefront's LDS writes visible with a release fence, and a copy
+// into LDS still in flight counts as such a write, so it waits for every
+// outstanding copy (vmcnt(0)) and no copy ever stays in flight across it.
+// Here the caller first waits for the copies the other wavefronts will read
+// (wait_vmem_le); the barrier completes this wavefront's LDS reads and writes
+// (lgkmcnt(0)) and the empty asm statements keep the compiler from moving
+// memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt not waited for
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // Wait until at most n (0..31, runtime, wave-uniform) vector memory operations
 // of this wavefront are outstanding.
 __device__ __forceinline__ void wait_vmem_le_rt(int n) {
