@@ -21,6 +21,11 @@
 // fragments come out of LDS transpose reads, and w is applied to the x
 // fragment in registers. Each wavefront owns one head and PT/WPH of its
 // 32-row p tiles against all N/32 n tiles.
+//
+// The block's dt travels with the first block's copies into a side tile, so
+// the weights w (and, fused, the in-chunk cumulative decay) are computed as
+// soon as that block has landed, without a round trip of their own; cs and
+// the states are stored at the end.
 #include "kernels.hpp"
 
 namespace ssd {
@@ -42,8 +47,10 @@ struct StateCfg {
     // ring of LDS blocks: three (two in flight while one is used) when two
     // workgroups still fit in a CU's LDS, else two. Two resident workgroups per
     // CU let one's stores and prologue overlap the other's copies and math.
-    static constexpr int NBUF = 2 * (3 * BUF + HPW * 256 * 4) <= 160 * 1024 ? 3 : 2;
-    static constexpr int LDS = NBUF * BUF + HPW * 256 * 4;   // + w vectors (Q <= 256)
+    // side tile: dt [HPW][Q], overwritten in place by w
+    static constexpr int SIDE = HPW * 256 * 4;
+    static constexpr int NBUF = 2 * (3 * BUF + SIDE) <= 160 * 1024 ? 3 : 2;
+    static constexpr int LDS = NBUF * BUF + SIDE;
     static constexpr int NDB = (kStateKB * BRC / 64 + 3) / 4;  // B copy instructions per wave
     static constexpr int NDX = (kStateKB * XRC / 64 + 3) / 4;  // x copy instructions per wave per head
 };
@@ -75,7 +82,17 @@ __device__ __forceinline__ void dma_issue(unsigned char* lds, const unsigned cha
     }
 }
 
-template <typename T, int PT, int NT, typename ST>
+// One 4-byte global -> LDS copy per lane: lane l writes LDS bytes
+// [lds + 4 l, lds + 4 l + 4).
+__device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t rs, uint32_t voff, unsigned char* lds) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 4, voff, 0, 0, 0);
+}
+
+constexpr uint32_t kOob = 0x80000000u;   // buffer offset past every range: the copy reads 0
+
+// FUSED: also compute (and write) cs from dt and A, the step of
+// ssd_chunk_cumsum; else read the given cs.
+template <typename T, int PT, int NT, typename ST, bool FUSED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void ssd_chunk_state_kernel(Params p) {
     using Cfg = StateCfg<T, PT, NT>;
     using V8 = typename Vec8<T>::type;
@@ -83,7 +100,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     constexpr int ESZ = (int)sizeof(T);
     __shared__ __attribute__((aligned(1024))) unsigned char smem[Cfg::LDS];
     constexpr int NBUF = Cfg::NBUF;
-    float* wv = reinterpret_cast<float*>(smem + NBUF * Cfg::BUF);   // [HPW][Q]
+    float* wv = reinterpret_cast<float*>(smem + NBUF * Cfg::BUF);   // [HPW][Q]: dt, then w
 
     const int Q = (int)p.chunk;
     const int64_t T_ = p.seqlen, H = p.nheads, P = p.headdim, N = p.dstate, G = p.ngroups;
@@ -106,58 +123,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // uniform per wavefront
     const int hf = lane >> 5, l32 = lane & 31;
 
-    // decay-to-chunk-end weights w_j for every head of the block
     const float* csbase = p.cs + ((b * H + h0) * nc + c) * Q;
     const float* dtbase = p.dt + tok0 * H + h0;
-    if (p.fuse_cs) {
-        // the in-chunk cumulative decay of head hq = wave (the step of
-        // ssd_chunk_cumsum, same arithmetic), written out for the later
-        // kernels and used here directly
-        const int per = Q >= 64 ? Q / 64 : 1, nact = Q / per;
-        if (wave < HPW) {
-            const int hq = wave;
-            float dtv[4], v[4];
-            const float Ah = hq < nh ? ldg(p.A + h0 + hq) : 0.0f;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int j = lane * per + k;
-                dtv[k] = (hq < nh && k < per && lane < nact && j < qc) ? ldg(dtbase + hq + (uint32_t)j * (uint32_t)H) : 0.0f;
-                {
-#pragma clang fp contract(off)
-                    v[k] = dtv[k] * Ah;   // a rounded product, as ssd_chunk_cumsum forms it
-                }
-            }
-            chunk_prefix(v, per, nact, qc, lane);
-            const float last = __shfl(v[per - 1], nact - 1, 64);
-            if (hq < nh && lane < nact) {
-                float* out = p.cs + ((b * H + h0 + hq) * nc + c) * Q + lane * per;
-                if (per == 4) {
-                    f32x4 o;
-                    o[0] = v[0]; o[1] = v[1]; o[2] = v[2]; o[3] = v[3];
-                    *reinterpret_cast<f32x4*>(out) = o;
-                } else {
-                    for (int k = 0; k < per; ++k) out[k] = v[k];
-                }
-            }
-            if (lane < nact) {
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    const int j = lane * per + k;
-                    if (k < per) wv[hq * Q + j] = (hq < nh && j < qc) ? exp2f((last - v[k]) * kLog2e) * dtv[k] : 0.0f;
-                }
-            }
-        }
-    } else {
-        for (int idx = threadIdx.x; idx < HPW * Q; idx += blockDim.x) {
-            const int hq = idx / Q, j = idx % Q;
-            float wj = 0.0f;
-            if (hq < nh && j < qc) {
-                const float* csr = csbase + (int64_t)hq * nc * Q;
-                wj = exp2f((ldg(csr + Q - 1) - ldg(csr + j)) * kLog2e) * ldg(dtbase + hq + (uint32_t)j * (uint32_t)H);
-            }
-            wv[hq * Q + j] = wj;
-        }
-    }
 
     const unsigned char* bbase = static_cast<const unsigned char*>(p.B) + (tok0 * G + g) * N * ESZ;
     const unsigned char* xbase = static_cast<const unsigned char*>(p.x) + (tok0 * H + h0) * P * ESZ;
@@ -166,6 +133,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     int offb[Cfg::NDB], offx[Cfg::NDX];
     dma_plan<Cfg::BRC, Cfg::NDB>(offb, bvalid, bstride, wave, lane);
     dma_plan<Cfg::XRC, Cfg::NDX>(offx, xvalid, xstride, wave, lane);
+    // side tile: lane value fi = (wave + 4i) * 64 + lane is (head fi / Q, token fi % Q)
+    const int srounds = (HPW * Q + 255) / 256;
+    auto issue_side = [&]() {
+        const __amdgpu_buffer_rsrc_t rd = raw_rsrc(dtbase);
+        for (int i = 0; i < srounds; ++i) {
+            const int fi = (wave + 4 * i) * 64 + lane, hq = fi / Q, j = fi - hq * Q;
+            const bool ok = hq < nh && j < qc;
+            dma4(rd, ok ? (uint32_t)(j * (int)H + hq) * 4u : kOob, reinterpret_cast<unsigned char*>(wv) + fi * 4);
+        }
+    };
     auto issue = [&](int blk, unsigned char* base) {
         const int r0 = blk * kStateKB;
         if (r0 + kStateKB <= qc) {          // full block: precomputed lane offsets
@@ -213,8 +190,54 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
     const int nblk = Q / kStateKB;
     constexpr int AHEAD = NBUF - 1;     // blocks in flight beyond the one in use
-    for (int k = 0; k < AHEAD && k < nblk; ++k) issue(k, smem + k * Cfg::BUF);
-    wait_vmem_le_rt(nblk > 1 && AHEAD > 1 ? per_block : 0);   // block 0 landed
+    const int hq = wave / WPH;   // = hh: the head this wavefront computes w for
+    float Ah = 0.0f;
+    if constexpr (FUSED) Ah = p.A[h0 + min(hq, nh - 1)];   // a scalar load, used after the first wait
+    for (int k = 0; k < AHEAD && k < nblk; ++k) {
+        issue(k, smem + k * Cfg::BUF);
+        if (k == 0) issue_side();
+    }
+    wait_vmem_le_rt(nblk > 1 && AHEAD > 1 ? per_block : 0);   // block 0 and the side tile landed
+    lds_barrier();
+
+    // decay-to-chunk-end weights w_j of head hq, computed by the head's first
+    // wavefront in place of its dt row. Fused: the in-chunk cumulative decay
+    // (the step of ssd_chunk_cumsum, same arithmetic) is formed here and kept
+    // for the store at the end.
+    const int per = Q >= 64 ? Q / 64 : 1, nact = Q / per;
+    float csv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (wave % WPH == 0) {
+        float* row = wv + hq * Q;
+        float dtv[4], v[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) dtv[k] = (k < per && lane < nact) ? row[lane * per + k] : 0.0f;
+        float last;
+        if constexpr (FUSED) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+#pragma clang fp contract(off)
+                v[k] = dtv[k] * Ah;   // a rounded product, as ssd_chunk_cumsum forms it
+            }
+            chunk_prefix(v, per, nact, qc, lane);
+            last = __shfl(v[per - 1], nact - 1, 64);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) csv[k] = v[k];
+        } else {
+            const float* csr = csbase + (int64_t)hq * nc * Q;
+            last = hq < nh ? ldg(csr + Q - 1) : 0.0f;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int j = lane * per + k;
+                v[k] = (hq < nh && k < per && lane < nact && j < qc) ? ldg(csr + j) : 0.0f;
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int j = lane * per + k;
+            if (k < per && lane < nact)
+                row[j] = (hq < nh && j < qc) ? exp2f((last - v[k]) * kLog2e) * dtv[k] : 0.0f;
+        }
+    }
     lds_barrier();
 
     // One block: start the copy of block blk + AHEAD into `next`, then run the
@@ -273,9 +296,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         lds_barrier();
     }
 
+    if (FUSED && wave % WPH == 0 && hh < nh && lane < nact) {
+        float* out = p.cs + ((b * H + h0 + hh) * nc + c) * Q + lane * per;
+        if (per == 4) {
+            f32x4 o;
+            o[0] = csv[0]; o[1] = csv[1]; o[2] = csv[2]; o[3] = csv[3];
+            *(__attribute__((address_space(1))) f32x4*)out = o;
+        } else {
+            for (int k = 0; k < per; ++k) out[k] = csv[k];
+        }
+    }
     if (active) {
-        // accumulator element r of tile (i, n): state row p = (pt0+i)*32 + lane%32,
-        // column n*32 + 8*(r/4) + 4*hf + r%4: four consecutive n per store
+        // accumulator element r of tile (i, n): state row p = (pt0+i)*32 + l32,
+        // column n*32 + 8*(r/4) + 4*hf + r%4. bf16: the lane halves swap the
+        // halves of quarters 2g and 2g+1 (v_permlane32_swap), so that a lane
+        // holds 8 consecutive columns (one 16-byte store); fp32: one quarter
+        // (4 columns) per store.
         const int64_t h = h0 + hh;
         ST* sg = static_cast<ST*>(p.states) + ((b * nc + c) * H + h) * P * N;   // [P][N] of this head
 #pragma unroll
@@ -283,21 +319,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             const int pr = (pt0 + i) * 32 + l32;
 #pragma unroll
             for (int n = 0; n < NT; ++n) {
+                if constexpr (sizeof(ST) == 2) {
 #pragma unroll
-                for (int gq = 0; gq < 4; ++gq) {
-                    const int col = n * 32 + 8 * gq + 4 * hf;
-                    if (pr < P && col < N) {
-                        ST* dst = sg + (uint32_t)(pr * (int)N + col);
-                        if constexpr (sizeof(ST) == 4) {
+                    for (int gp = 0; gp < 2; ++gp) {
+                        uint32_t w[2][2];
+#pragma unroll
+                        for (int q = 0; q < 2; ++q) {
+                            const int gq = 2 * gp + q;
+                            bf16x4 v;
+#pragma unroll
+                            for (int r = 0; r < 4; ++r) v[r] = from_f32<bf16>(acc[i][n][4 * gq + r]);
+                            const u32x2 u = __builtin_bit_cast(u32x2, v);
+                            w[q][0] = u[0];
+                            w[q][1] = u[1];
+                        }
+#pragma unroll
+                        for (int k = 0; k < 2; ++k) {
+                            const auto sw = __builtin_amdgcn_permlane32_swap(w[0][k], w[1][k], false, false);
+                            w[0][k] = sw[0];
+                            w[1][k] = sw[1];
+                        }
+                        const int col = n * 32 + 8 * (2 * gp + hf);
+                        if (pr < P && col < N) {
+                            u32x4 o;
+                            o[0] = w[0][0]; o[1] = w[0][1]; o[2] = w[1][0]; o[3] = w[1][1];
+                            *(__attribute__((address_space(1))) u32x4*)(sg + (uint32_t)(pr * (int)N + col)) = o;
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int gq = 0; gq < 4; ++gq) {
+                        const int col = n * 32 + 8 * gq + 4 * hf;
+                        if (pr < P && col < N) {
                             f32x4 v;
                             v[0] = acc[i][n][4 * gq]; v[1] = acc[i][n][4 * gq + 1];
                             v[2] = acc[i][n][4 * gq + 2]; v[3] = acc[i][n][4 * gq + 3];
-                            *(__attribute__((address_space(1))) f32x4*)dst = v;
-                        } else {
-                            bf16x4 v;
-                            v[0] = from_f32<bf16>(acc[i][n][4 * gq]); v[1] = from_f32<bf16>(acc[i][n][4 * gq + 1]);
-                            v[2] = from_f32<bf16>(acc[i][n][4 * gq + 2]); v[3] = from_f32<bf16>(acc[i][n][4 * gq + 3]);
-                            *(__attribute__((address_space(1))) bf16x4*)dst = v;
+                            *(__attribute__((address_space(1))) f32x4*)(sg + (uint32_t)(pr * (int)N + col)) = v;
                         }
                     }
                 }
@@ -311,7 +368,10 @@ static hipError_t launch_cs(const Params& p, hipStream_t s) {
     using Cfg = StateCfg<T, PT, NT>;
     const int64_t nhb = (p.heads_per_group + Cfg::HPW - 1) / Cfg::HPW;
     dim3 grid((unsigned)(p.nchunks * p.ngroups * nhb), (unsigned)p.batch);
-    hipLaunchKernelGGL((ssd_chunk_state_kernel<T, PT, NT, ST>), grid, dim3(256), 0, s, p);
+    if (p.fuse_cs)
+        hipLaunchKernelGGL((ssd_chunk_state_kernel<T, PT, NT, ST, true>), grid, dim3(256), 0, s, p);
+    else
+        hipLaunchKernelGGL((ssd_chunk_state_kernel<T, PT, NT, ST, false>), grid, dim3(256), 0, s, p);
     return hipGetLastError();
 }
 

@@ -103,13 +103,23 @@ __device__ __forceinline__ f32x16 zero16() {
 
 // ---- wavefront prefix sum --------------------------------------------------
 
-// Inclusive prefix sum of v over the 64 lanes of a wavefront (Hillis-Steele).
+// Inclusive prefix sum of v over the 64 lanes of a wavefront with DPP: a
+// Hillis-Steele scan inside each 16-lane row (row_shr 1, 2, 4, 8; lanes
+// shifted in from outside the row add 0), then row 0's total is added to row
+// 1 and row 2's to row 3 (row_bcast:15), then the total of rows 0-1 to rows 2
+// and 3 (row_bcast:31).
+template <int CTRL, int ROW_MASK, bool BOUND>
+__device__ __forceinline__ float dpp_f32(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xF, BOUND));
+}
 __device__ __forceinline__ float wave_inclusive_scan(float v, int lane) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const float n = __shfl_up(v, off, 64);
-        if (lane >= off) v += n;
-    }
+    (void)lane;
+    v += dpp_f32<0x111, 0xF, true>(v);    // row_shr:1
+    v += dpp_f32<0x112, 0xF, true>(v);    // row_shr:2
+    v += dpp_f32<0x114, 0xF, true>(v);    // row_shr:4
+    v += dpp_f32<0x118, 0xF, true>(v);    // row_shr:8
+    v += dpp_f32<0x142, 0xA, false>(v);   // row_bcast:15 into rows 1 and 3
+    v += dpp_f32<0x143, 0xC, false>(v);   // row_bcast:31 into rows 2 and 3
     return v;
 }
 
@@ -380,20 +390,19 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
-// Wait until at most n (0..31, runtime, wave-uniform) vector memory operations
-// of this wavefront are outstanding.
+// Wait until at most n (runtime, wave-uniform) vector memory operations of
+// this wavefront are outstanding; n above the counter's range (63) waits for
+// at most 63, i.e. for more than asked.
 __device__ __forceinline__ void wait_vmem_le_rt(int n) {
     switch (n) {
 #define SSD_WAIT_CASE(K) case K: wait_vmem_le<K>(); break;
-        SSD_WAIT_CASE(0) SSD_WAIT_CASE(1) SSD_WAIT_CASE(2) SSD_WAIT_CASE(3) SSD_WAIT_CASE(4)
-        SSD_WAIT_CASE(5) SSD_WAIT_CASE(6) SSD_WAIT_CASE(7) SSD_WAIT_CASE(8) SSD_WAIT_CASE(9)
-        SSD_WAIT_CASE(10) SSD_WAIT_CASE(11) SSD_WAIT_CASE(12) SSD_WAIT_CASE(13) SSD_WAIT_CASE(14)
-        SSD_WAIT_CASE(15) SSD_WAIT_CASE(16) SSD_WAIT_CASE(17) SSD_WAIT_CASE(18) SSD_WAIT_CASE(19)
-        SSD_WAIT_CASE(20) SSD_WAIT_CASE(21) SSD_WAIT_CASE(22) SSD_WAIT_CASE(23) SSD_WAIT_CASE(24)
-        SSD_WAIT_CASE(25) SSD_WAIT_CASE(26) SSD_WAIT_CASE(27) SSD_WAIT_CASE(28) SSD_WAIT_CASE(29)
-        SSD_WAIT_CASE(30) SSD_WAIT_CASE(31)
+#define SSD_WAIT_8(K) SSD_WAIT_CASE(K) SSD_WAIT_CASE(K + 1) SSD_WAIT_CASE(K + 2) SSD_WAIT_CASE(K + 3) \
+    SSD_WAIT_CASE(K + 4) SSD_WAIT_CASE(K + 5) SSD_WAIT_CASE(K + 6) SSD_WAIT_CASE(K + 7)
+        SSD_WAIT_8(0) SSD_WAIT_8(8) SSD_WAIT_8(16) SSD_WAIT_8(24)
+        SSD_WAIT_8(32) SSD_WAIT_8(40) SSD_WAIT_8(48) SSD_WAIT_8(56)
+#undef SSD_WAIT_8
 #undef SSD_WAIT_CASE
-        default: wait_vmem(); break;
+        default: wait_vmem_le<63>(); break;
     }
 }
 
