@@ -545,15 +545,27 @@ static hipError_t launch_sc2(const Params& p, int hpw, int lds, hipStream_t s) {
     return hipGetLastError();
 }
 
-// heads per workgroup: amortise phase A over up to 8 heads while keeping at
-// least ~512 workgroups in flight.
+// Heads per workgroup. Phase A (C B^T of the chunk, about 1.6 heads' worth of
+// work) is paid once per workgroup, so more heads per workgroup amortise it,
+// but the workgroups should fill the compute units in whole rounds (one
+// workgroup per compute unit at a time). Minimise rounds x (1.6 + the most
+// heads any workgroup takes).
 static int scan_hpw(const Params& p) {
-    const int64_t units = p.batch * p.nchunks * p.nheads;
-    int64_t hpw = units / 512;
-    if (hpw > 8) hpw = 8;
-    if (hpw > p.heads_per_group) hpw = p.heads_per_group;
-    if (hpw < 1) hpw = 1;
-    return (int)hpw;
+    const int64_t cus = device_cus();
+    const int64_t chunks = p.batch * p.nchunks * p.ngroups, hpg = p.heads_per_group;
+    int best = 1;
+    double best_cost = 1e300;
+    for (int64_t h = 1; h <= hpg && h <= 64; ++h) {
+        const int64_t nhb = (hpg + h - 1) / h;
+        const int64_t most = (hpg + nhb - 1) / nhb;
+        const int64_t rounds = (chunks * nhb + cus - 1) / cus;
+        const double cost = (double)rounds * (1.6 + (double)most);
+        if (cost < best_cost - 1e-9) {
+            best_cost = cost;
+            best = (int)h;
+        }
+    }
+    return best;
 }
 
 template <typename T, int PT, int NT, typename ST>
