@@ -170,7 +170,15 @@ def record_traffic(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, workload,
         if "state_passing" in name:
             return "bf16" if ("IDF16bEE" in name or "<__bf16>" in name) else "fp32"
         m = re.search(r"Li\d+ELi\d+E(DF16b|f)", name)
-        return None if m is None else {"DF16b": "bf16", "f": "fp32"}[m.group(1)]
+        if m is not None:
+            return {"DF16b": "bf16", "f": "fp32"}[m.group(1)]
+        # the profiler's demangler garbles some of these names; the state
+        # type argument survives as "EDF1..." (bf16) or "EfL..." (fp32)
+        if "EDF1" in name:
+            return "bf16"
+        if "EfL" in name:
+            return "fp32"
+        return None
 
     for kern in KERNELS:
         names = [k for k in fe if kern + "_kernel" in k]
@@ -215,7 +223,7 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=100)   # ~40 ms: clocks settle before timing
     ap.add_argument("--workload", default="m2p7")
     ap.add_argument("--state-dtype", default=None, choices=["fp32", "bf16"],
                     help="storage of the inter-chunk states (default: bf16 for bf16 inputs); the "
