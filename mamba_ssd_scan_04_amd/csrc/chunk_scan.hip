@@ -114,6 +114,9 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
     const int RT = Q / 32;
     const int rt = RT == 8 ? (wave < 4 ? wave : 11 - wave) : (wave < RT ? wave : -1);
     const bool active = rt >= 0;
+    // the heavier row tiles (the longer chain of key tiles per head) get issue
+    // priority over their SIMD partner, which fills the gaps they leave
+    if (rt >= 4) __builtin_amdgcn_s_setprio(1);
 
     const uint32_t bcs = (uint32_t)(G * N);
     const T* cbase = static_cast<const T*>(p.C) + (tok0 * G + g) * N;
