@@ -57,7 +57,7 @@ def _load():
             build(force=True)
         lib = ctypes.CDLL(_LIB)
         i64, dp = ctypes.c_int64, ctypes.POINTER(ctypes.c_double)
-        lib.ssd_oracle_forward.argtypes = [i64] * 6 + [dp] * 6 + [dp, dp, i64, dp, ctypes.c_int]
+        lib.ssd_oracle_forward.argtypes = [i64] * 6 + [dp] * 6 + [dp, dp, dp, i64, dp, ctypes.c_int]
         lib.ssd_oracle_forward.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -76,14 +76,17 @@ def default_threads() -> int:
         return os.cpu_count() or 1
 
 
-def recurrence(x, dt, A, B, C, D, snap_every: int = 0, nthreads: int | None = None):
+def recurrence(x, dt, A, B, C, D, snap_every: int = 0, nthreads: int | None = None, init=None):
     """Knowl 1 linear form, fp64. Returns (y, final[, snaps]).
 
     x [b,T,H,P], dt [b,T,H], A [H], B/C [b,T,G,N], D [H] (any float arrays;
-    converted to contiguous float64). final is [b,H,N,P]. With snap_every=Q,
-    also returns snaps [b,nc,H,N,P]: the state entering each chunk of Q tokens.
+    converted to contiguous float64). final is [b,H,N,P]. init [b,H,N,P] is
+    the state before the first token (None: zero). With snap_every=Q, also
+    returns snaps [b,nc,H,N,P]: the state entering each chunk of Q tokens.
     """
     x, dt, A, B, C, D = (np.ascontiguousarray(v, dtype=np.float64) for v in (x, dt, A, B, C, D))
+    if init is not None:
+        init = np.ascontiguousarray(init, dtype=np.float64)
     b, T, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
     y = np.empty_like(x)
@@ -92,8 +95,10 @@ def recurrence(x, dt, A, B, C, D, snap_every: int = 0, nthreads: int | None = No
     if snap_every > 0:
         nc = -(-T // snap_every)
         snaps = np.empty((b, nc, H, N, P))
+    if init is not None and init.shape != (b, H, N, P):
+        raise ValueError(f"init must be [b,H,N,P] = {(b, H, N, P)}, got {init.shape}")
     rc = _load().ssd_oracle_forward(b, T, H, P, N, G, _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
-                                    _ptr(C), _ptr(D), _ptr(y), _ptr(final), snap_every,
+                                    _ptr(C), _ptr(D), _ptr(init), _ptr(y), _ptr(final), snap_every,
                                     _ptr(snaps), nthreads or default_threads())
     if rc != 0:
         raise RuntimeError(f"ssd_oracle_forward failed with code {rc}")
@@ -132,7 +137,7 @@ def quadratic(x, dt, A, B, C, D):
     return y
 
 
-def chunked(x, dt, A, B, C, D, Q: int):
+def chunked(x, dt, A, B, C, D, Q: int, init=None):
     """Knowl 2 block decomposition in fp64, steps in the pages' order.
 
     Returns a dict:
@@ -142,7 +147,7 @@ def chunked(x, dt, A, B, C, D, Q: int):
                          cumulative products); entries past a ragged chunk's
                          end are NaN
       S      [b,nc,H,N,P] right-factor chunk states B^T (decayed X)
-      h_in   [b,nc,H,N,P] state entering each chunk (h_c, h_0 = 0)
+      h_in   [b,nc,H,N,P] state entering each chunk (h_c; h_0 = init, zero if None)
     Reading of "decayed X": token j of a chunk is weighted by the decay from j
     to the chunk's end, a_{j+1} ... a_{Q-1}; of "decayed h_c": row j is scaled
     by a_0 ... a_j. A last chunk shorter than Q is allowed.
@@ -179,7 +184,7 @@ def chunked(x, dt, A, B, C, D, Q: int):
         S[:, c] = np.einsum("bhj,bjhn,bjhp->bhnp", w, Bh[:, t0:t1], xin[:, t0:t1])
     # step 4: inter-chunk recurrence on chunk states
     h_in = np.zeros((b, nc, H, N, P))
-    state = np.zeros((b, H, N, P))
+    state = np.zeros((b, H, N, P)) if init is None else np.array(init, dtype=np.float64)
     for c, (t0, t1, cs) in enumerate(seg):
         h_in[:, c] = state
         state = np.exp(cs[:, -1, :])[:, :, None, None] * state + S[:, c]

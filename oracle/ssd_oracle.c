@@ -11,7 +11,7 @@
  * scaled by dt_t, and a skip term D_h * x_t):
  *
  *   for every batch element b and head h, with group g = h / (H / G):
- *     state_{-1} = 0                                   (N x P)
+ *     state_{-1} = init[b,h] (zero when no initial state is given)   (N x P)
  *     state_t    = exp(dt[b,t,h] * A[h]) * state_{t-1}
  *                  + dt[b,t,h] * B[b,t,g,:] (outer) x[b,t,h,:]
  *     y[b,t,h,:] = C[b,t,g,:]^T state_t + D[h] * x[b,t,h,:]
@@ -23,9 +23,9 @@
  * pattern), assigned contiguously.
  *
  * Layouts (row-major, contiguous): x, y [b,T,H,P]; dt [b,T,H]; A, D [H];
- * B, C [b,T,G,N]; final [b,H,N,P]. Optional boundary snapshots
+ * B, C [b,T,G,N]; final and init [b,H,N,P]. Optional boundary snapshots
  * snaps [b,nc,H,N,P], nc = ceil(T / every): snaps[c] is the state after token
- * c*every - 1, i.e. the state entering chunk c (zero for c = 0).
+ * c*every - 1, i.e. the state entering chunk c (the initial state for c = 0).
  *
  * Parallelism: a pool of POSIX threads takes (b, h) items from a shared
  * counter. Each item is independent; results do not depend on the thread
@@ -39,7 +39,7 @@
 
 typedef struct {
     int64_t batch, seqlen, nheads, headdim, dstate, ngroups, every;
-    const double *x, *dt, *A, *B, *C, *D;
+    const double *x, *dt, *A, *B, *C, *D, *init;
     double *y, *final_state, *snaps;
     int64_t next;      /* shared work counter */
     int failed;
@@ -51,7 +51,10 @@ static void run_item(job_t* j, int64_t item, double* st) {
     const int64_t b = item / H, h = item % H;
     const int64_t g = h / (H / G);
     const double Ah = j->A[h], Dh = j->D[h];
-    memset(st, 0, sizeof(double) * (size_t)(N * P));
+    if (j->init)
+        memcpy(st, j->init + ((b * H + h) * N) * P, sizeof(double) * (size_t)(N * P));
+    else
+        memset(st, 0, sizeof(double) * (size_t)(N * P));
     for (int64_t t = 0; t < T; ++t) {
         if (j->snaps && t % j->every == 0) {
             const int64_t nc = (T + j->every - 1) / j->every;
@@ -98,26 +101,32 @@ static void* worker(void* arg) {
 }
 
 /* Returns 0 on success, -1 on bad arguments, -2 on allocation/thread failure.
- * y and x may not alias. final_state and snaps may be NULL. every <= 0 turns
- * the snapshots off. nthreads < 1 means 1. */
+ * y and x may not alias. init, final_state and snaps may be NULL (init NULL:
+ * zero initial state). every <= 0 turns the snapshots off. nthreads < 1
+ * means 1. */
 int ssd_oracle_forward(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
                        int64_t dstate, int64_t ngroups, const double* x, const double* dt,
                        const double* A, const double* B, const double* C, const double* D,
-                       double* y, double* final_state, int64_t every, double* snaps,
-                       int nthreads) {
+                       const double* init, double* y, double* final_state, int64_t every,
+                       double* snaps, int nthreads) {
     if (batch < 0 || seqlen < 0 || nheads <= 0 || headdim <= 0 || dstate <= 0 ||
         ngroups <= 0 || nheads % ngroups != 0)
         return -1;
     if (!x || !dt || !A || !B || !C || !D || !y) return -1;
     if (batch == 0 || seqlen == 0) {
-        if (final_state && batch > 0)
-            memset(final_state, 0, sizeof(double) * (size_t)(batch * nheads * dstate * headdim));
+        if (final_state && batch > 0) {
+            const size_t n = (size_t)(batch * nheads * dstate * headdim);
+            if (init)
+                memcpy(final_state, init, sizeof(double) * n);
+            else
+                memset(final_state, 0, sizeof(double) * n);
+        }
         return 0;
     }
     job_t j;
     j.batch = batch; j.seqlen = seqlen; j.nheads = nheads; j.headdim = headdim;
     j.dstate = dstate; j.ngroups = ngroups; j.every = every;
-    j.x = x; j.dt = dt; j.A = A; j.B = B; j.C = C; j.D = D;
+    j.x = x; j.dt = dt; j.A = A; j.B = B; j.C = C; j.D = D; j.init = init;
     j.y = y; j.final_state = final_state; j.snaps = (every > 0) ? snaps : NULL;
     j.next = 0; j.failed = 0;
     if (nthreads < 1) nthreads = 1;

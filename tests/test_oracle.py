@@ -255,6 +255,84 @@ def test_thread_count_does_not_change_results(oracle_mod):
     assert np.array_equal(y1, y8) and np.array_equal(f1, f8)
 
 
+# ---- initial state ("Transformers are SSMs", Knowl 1: the recurrence starts
+# from h_{-1}; the pages take it as zero, the library also accepts a given one)
+
+def _split(inp, t0, t1):
+    return {k: (v[:, t0:t1] if k in ("x", "dt", "B", "C") else v) for k, v in inp.items()}
+
+
+def test_initial_state_split_resume(oracle_mod):
+    """Running tokens [T1, T) from the state after [0, T1) continues the full
+    run exactly: the initial state is the state before the first token."""
+    rng = np.random.default_rng(20)
+    inp = rand_inputs(rng, 2, 40, 3, 4, 5, 1, a_scale=0.2)
+    y, fin = rec(oracle_mod, inp)
+    for t1 in (1, 17, 39):
+        y1, f1 = rec(oracle_mod, _split(inp, 0, t1))
+        y2, f2 = rec(oracle_mod, _split(inp, t1, 40), init=f1)
+        assert oracle_mod.rel_err(y2, y[:, t1:]) < 1e-12
+        assert oracle_mod.rel_err(f2, fin) < 1e-12
+        np.testing.assert_array_equal(y1, y[:, :t1])
+
+
+def test_initial_state_free_response_closed_form(oracle_mod):
+    """With x = 0 the output is the initial state's free decay read out by C:
+    y_t = C_t^T exp(A sum_{s<=t} dt_s) h_init, final = exp(A sum_s dt_s) h_init
+    (written from the closed form, not from the recurrence)."""
+    rng = np.random.default_rng(21)
+    b, T, H, P, N, G = 2, 9, 4, 3, 5, 2
+    inp = rand_inputs(rng, b, T, H, P, N, G)
+    inp["x"] = np.zeros_like(inp["x"])
+    init = rng.standard_normal((b, H, N, P))
+    y, fin = rec(oracle_mod, inp, init=init)
+    hpg = H // G
+    for bi in range(b):
+        for h in range(H):
+            g = h // hpg
+            lam = np.cumsum(inp["dt"][bi, :, h]) * inp["A"][h]
+            for t in range(T):
+                ref = np.exp(lam[t]) * (inp["C"][bi, t, g] @ init[bi, h])
+                np.testing.assert_allclose(y[bi, t, h], ref, rtol=1e-13, atol=1e-15)
+            np.testing.assert_allclose(fin[bi, h], np.exp(lam[-1]) * init[bi, h], rtol=1e-13, atol=1e-15)
+
+
+def test_initial_state_superposition(oracle_mod):
+    """The output is affine in the initial state: y(init) - y(0) is the
+    free response of init alone (x = 0), for any inputs."""
+    rng = np.random.default_rng(22)
+    inp = rand_inputs(rng, 1, 21, 2, 4, 3, 1)
+    init = rng.standard_normal((1, 2, 3, 4))
+    y0, f0 = rec(oracle_mod, inp)
+    y1, f1 = rec(oracle_mod, inp, init=init)
+    free = dict(inp, x=np.zeros_like(inp["x"]))
+    yf, ff = rec(oracle_mod, free, init=init)
+    assert oracle_mod.rel_err(y1 - y0, yf) < 1e-11
+    assert oracle_mod.rel_err(f1 - f0, ff) < 1e-11
+
+
+def test_chunked_with_initial_state_matches_recurrence(oracle_mod):
+    rng = np.random.default_rng(23)
+    inp = rand_inputs(rng, 2, 37, 3, 4, 5, 1, a_scale=0.3)
+    init = rng.standard_normal((2, 3, 5, 4))
+    y, fin, snaps = rec(oracle_mod, inp, snap_every=8, init=init)
+    np.testing.assert_array_equal(snaps[:, 0], init)
+    for Q in (1, 5, 8, 37):
+        out = oracle_mod.chunked(**inp, Q=Q, init=init)
+        assert oracle_mod.rel_err(out["y"], y) < 1e-12
+        assert oracle_mod.rel_err(out["final"], fin) < 1e-12
+        np.testing.assert_array_equal(out["h_in"][:, 0], init)
+
+
+def test_initial_state_with_empty_sequence(oracle_mod):
+    rng = np.random.default_rng(24)
+    inp = rand_inputs(rng, 2, 0, 2, 3, 4, 1)
+    init = rng.standard_normal((2, 2, 4, 3))
+    y, fin = rec(oracle_mod, inp, init=init)
+    assert y.shape == (2, 0, 2, 3)
+    np.testing.assert_array_equal(fin, init)
+
+
 MUTANTS = {
     "dropped_skip": ("yt[p] = Dh * xt[p];", "yt[p] = 0.0;"),
     "dropped_dt_input": ("const double u = dtv * Bt[n];", "const double u = Bt[n];"),
@@ -263,6 +341,8 @@ MUTANTS = {
     "wrong_group_map": ("const int64_t g = h / (H / G);", "const int64_t g = h % G;"),
     # y_t read from the state before token t enters it (exclusive mask product)
     "stale_state_output": None,
+    # the given initial state ignored (zero start)
+    "ignored_initial_state": ("    if (j->init)\n        memcpy(st,", "    if (0)\n        memcpy(st,"),
 }
 
 UPDATE_BLOCK = """        for (int64_t n = 0; n < N; ++n) {
@@ -303,18 +383,19 @@ def test_planted_mistakes_are_caught(oracle_mod, name):
                         lpath, "-lm"], check=True)
         lib = ctypes.CDLL(lpath)
         i64, dp = ctypes.c_int64, ctypes.POINTER(ctypes.c_double)
-        lib.ssd_oracle_forward.argtypes = [i64] * 6 + [dp] * 6 + [dp, dp, i64, dp, ctypes.c_int]
+        lib.ssd_oracle_forward.argtypes = [i64] * 6 + [dp] * 6 + [dp, dp, dp, i64, dp, ctypes.c_int]
 
-        def run(inp):
+        def run(inp, init=None, with_final=False):
             x, dt, A, B, C, D = (np.ascontiguousarray(inp[k], dtype=np.float64)
                                  for k in ("x", "dt", "A", "B", "C", "D"))
             b, T, H, P = x.shape
             y = np.empty_like(x)
             fin = np.empty((b, H, B.shape[3], P))
             pp = lambda a: a.ctypes.data_as(dp)
+            ini = None if init is None else pp(np.ascontiguousarray(init, dtype=np.float64))
             lib.ssd_oracle_forward(b, T, H, P, B.shape[3], B.shape[2], pp(x), pp(dt), pp(A),
-                                   pp(B), pp(C), pp(D), pp(y), pp(fin), 0, None, 1)
-            return y
+                                   pp(B), pp(C), pp(D), ini, pp(y), pp(fin), 0, None, 1)
+            return (y, fin) if with_final else y
 
         with open(os.path.join(HERE, "golden", "hand_example_T3.json")) as f:
             g = json.load(f)
@@ -323,6 +404,11 @@ def test_planted_mistakes_are_caught(oracle_mod, name):
         rng = np.random.default_rng(12)
         inp = rand_inputs(rng, 1, 12, 4, 3, 4, 2)
         dual_ok = oracle_mod.rel_err(run(inp), oracle_mod.quadratic(**inp)) < 1e-12
-        assert not (golden_ok and dual_ok), f"planted mistake {name} was not caught"
+        # split/resume: the second half from the first half's final state
+        yfull = run(inp)
+        _, f1 = run(_split(inp, 0, 5), with_final=True)
+        y2 = run(_split(inp, 5, 12), init=f1)
+        resume_ok = oracle_mod.rel_err(y2, yfull[:, 5:]) < 1e-12
+        assert not (golden_ok and dual_ok and resume_ok), f"planted mistake {name} was not caught"
     finally:
         shutil.rmtree(tmp)
