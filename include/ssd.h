@@ -114,6 +114,20 @@ ssd_status ssd_forward(const ssd_dims* d, const void* x, const float* dt, const 
                        hipStream_t stream);
 
 /*
+ * Full forward from a given initial state: the recurrence of Knowl 1 started
+ * at h_{-1} = initial_state instead of zero (so that a sequence can be resumed
+ * from the final state of its prefix). initial_state [b,H,N,P] fp32 (device,
+ * caller-owned, read only; 16-byte aligned), or NULL for a zero state, which
+ * gives exactly ssd_forward. Enqueues ssd_chunk_cumsum_state,
+ * ssd_state_passing_init and ssd_chunk_scan_init. With T = 0, final_state
+ * receives a copy of initial_state. Other arguments and errors as ssd_forward.
+ */
+ssd_status ssd_forward_init(const ssd_dims* d, const void* x, const float* dt, const float* A,
+                            const void* B, const void* C, const float* D, const float* initial_state,
+                            void* y, float* final_state, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
+/*
  * Stage 1 (Knowl 2, "intra-chunk cumulative products of A", taken in log
  * space): cs[b,h,c,j] = sum_{s=0..j} dt[b,cQ+s,h] * A[h], an inclusive prefix
  * sum per chunk, so exp(cs) is the cumulative product of a. Positions past the
@@ -152,6 +166,13 @@ ssd_status ssd_state_passing(const ssd_dims* d, const float* cs, void* states,
                              float* final_state, hipStream_t stream);
 
 /*
+ * Stage 3 from a given initial state: as ssd_state_passing with h_0 =
+ * initial_state [b,H,N,P] fp32 (NULL: zero), so states[c = 0] receives h_0.
+ */
+ssd_status ssd_state_passing_init(const ssd_dims* d, const float* cs, void* states,
+                                  const float* initial_state, float* final_state, hipStream_t stream);
+
+/*
  * Stage 4 (Knowl 2, diagonal-block outputs (L o C B^T) X, the off-diagonal
  * output C (decayed h_c) and their sum; plus D * x):
  *   y[t=cQ+j] = sum_{i<=j} (C_j . B_i) exp(cs_j - cs_i) dt_i x_i
@@ -161,6 +182,16 @@ ssd_status ssd_state_passing(const ssd_dims* d, const float* cs, void* states,
 ssd_status ssd_chunk_scan(const ssd_dims* d, const void* x, const float* dt, const void* B,
                           const void* C, const float* D, const float* cs, const void* states,
                           void* y, hipStream_t stream);
+
+/*
+ * Stage 4 for a nonzero initial state: as ssd_chunk_scan, but the first
+ * chunk's carried-state term exp(cs_j) C_j^T h_0 is applied as well, with h_0
+ * read from states[c = 0] as ssd_state_passing_init wrote it. (ssd_chunk_scan
+ * takes h_0 = 0 and does not read it.)
+ */
+ssd_status ssd_chunk_scan_init(const ssd_dims* d, const void* x, const float* dt, const void* B,
+                               const void* C, const float* D, const float* cs, const void* states,
+                               void* y, hipStream_t stream);
 
 #ifdef __cplusplus
 }

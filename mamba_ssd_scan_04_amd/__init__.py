@@ -64,13 +64,18 @@ def load_library() -> ctypes.CDLL:
     lib.ssd_stage_sizes.restype = st
     lib.ssd_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.ssd_forward.restype = st
+    lib.ssd_forward_init.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.ssd_forward_init.restype = st
     lib.ssd_chunk_cumsum.argtypes, lib.ssd_chunk_cumsum.restype = [P, vp, vp, vp, vp], st
     lib.ssd_chunk_state.argtypes, lib.ssd_chunk_state.restype = [P, vp, vp, vp, vp, vp, vp], st
     lib.ssd_chunk_cumsum_state.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
     lib.ssd_chunk_cumsum_state.restype = st
     lib.ssd_state_passing.argtypes, lib.ssd_state_passing.restype = [P, vp, vp, vp, vp], st
+    lib.ssd_state_passing_init.argtypes, lib.ssd_state_passing_init.restype = [P, vp, vp, vp, vp, vp], st
     lib.ssd_chunk_scan.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.ssd_chunk_scan.restype = st
+    lib.ssd_chunk_scan_init.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.ssd_chunk_scan_init.restype = st
     _lib = lib
     return lib
 
@@ -148,6 +153,14 @@ def ssd_forward(d, x, dt, A, B, C, D, y, final_state, workspace, workspace_bytes
                                       _ptr(workspace), workspace_bytes, s))
 
 
+def ssd_forward_init(d, x, dt, A, B, C, D, initial_state, y, final_state, workspace, workspace_bytes,
+                     stream=None):
+    s = _stream(final_state.device) if stream is None else stream
+    _check(load_library().ssd_forward_init(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
+                                           _ptr(C), _ptr(D), _ptr(initial_state), _ptr(y),
+                                           _ptr(final_state), _ptr(workspace), workspace_bytes, s))
+
+
 def ssd_chunk_cumsum(d, dt, A, cs, stream=None):
     s = _stream(dt.device) if stream is None else stream
     _check(load_library().ssd_chunk_cumsum(ctypes.byref(d), _ptr(dt), _ptr(A), _ptr(cs), s))
@@ -171,6 +184,18 @@ def ssd_state_passing(d, cs, states, final_state, stream=None):
                                             _ptr(final_state), s))
 
 
+def ssd_state_passing_init(d, cs, states, initial_state, final_state, stream=None):
+    s = _stream(final_state.device) if stream is None else stream
+    _check(load_library().ssd_state_passing_init(ctypes.byref(d), _ptr(cs), _ptr(states),
+                                                 _ptr(initial_state), _ptr(final_state), s))
+
+
+def ssd_chunk_scan_init(d, x, dt, B, C, D, cs, states, y, stream=None):
+    s = _stream(x.device) if stream is None else stream
+    _check(load_library().ssd_chunk_scan_init(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(B), _ptr(C),
+                                              _ptr(D), _ptr(cs), _ptr(states), _ptr(y), s))
+
+
 def ssd_chunk_scan(d, x, dt, B, C, D, cs, states, y, stream=None):
     s = _stream(x.device) if stream is None else stream
     _check(load_library().ssd_chunk_scan(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(B), _ptr(C),
@@ -188,8 +213,10 @@ def alloc_workspace(d: SsdDims, device) -> torch.Tensor:
     return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
 
 
-def forward(x, dt, A, B, C, D, chunk_size: int, state_dtype: str | None = None, workspace=None):
-    """y, final_state = SSD(x, dt, A, B, C, D) through ssd_forward.
+def forward(x, dt, A, B, C, D, chunk_size: int, state_dtype: str | None = None, workspace=None,
+            initial_state=None):
+    """y, final_state = SSD(x, dt, A, B, C, D) through ssd_forward (or
+    ssd_forward_init when initial_state [b,H,N,P] fp32 is given).
 
     state_dtype is the storage of the inter-chunk states in the workspace
     ("fp32" or "bf16"; default: that of x). The running state and the returned
@@ -202,7 +229,12 @@ def forward(x, dt, A, B, C, D, chunk_size: int, state_dtype: str | None = None, 
     final = torch.empty((d.batch, d.nheads, d.dstate, d.headdim), dtype=torch.float32, device=x.device)
     if workspace is None:
         workspace = alloc_workspace(d, x.device)
-    ssd_forward(d, x, dt, A, B, C, D, y, final, workspace, workspace.numel())
+    if initial_state is None:
+        ssd_forward(d, x, dt, A, B, C, D, y, final, workspace, workspace.numel())
+    else:
+        if initial_state.dtype != torch.float32 or tuple(initial_state.shape) != tuple(final.shape):
+            raise ValueError(f"initial_state must be float32 {tuple(final.shape)}")
+        ssd_forward_init(d, x, dt, A, B, C, D, initial_state, y, final, workspace, workspace.numel())
     return y, final
 
 

@@ -105,6 +105,7 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
     const int64_t t0 = (int64_t)c * Q;
     const int qc = (int)min<int64_t>(Q, T_ - t0);
     const int64_t tok0 = b * T_ + t0;            // first token row of the chunk
+    const bool hc = c > 0 || p.read_h0 != 0;     // a carried state enters this chunk
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -183,7 +184,7 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
     if (nh > 0) {   // head 0's tiles start moving before phase A
         load_vec(0);
         if (NBX == 2 || !bstage) issue_x(0, smem);
-        if (c > 0) issue_h(0, hb0);
+        if (hc) issue_h(0, hb0);
     }
 
     const int nlast = (int)N - 8;
@@ -322,7 +323,7 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
         if (more) {
             load_vec(hh + 1);   // before the copies: its results are waited for without them
             if (NBX == 2) issue_x(hh + 1, xn);
-            if (NBH == 2 && c > 0) issue_h(hh + 1, hn);
+            if (NBH == 2 && hc) issue_h(hh + 1, hn);
         }
         bool stored_all = true;
         if (active) {
@@ -398,7 +399,7 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
             // them issued) before stage k computes; the scheduling barriers
             // keep the compiler from sinking those reads into their uses
             Stage sa, sb;
-            if (c > 0) {   // (h_c^T C^T), then scaled by exp(cs_j)
+            if (hc) {   // (h_c^T C^T), then scaled by exp(cs_j)
                 typename Vec8<ST>::type hv[KS / 2][PT];
 #pragma unroll
                 for (int half = 0; half < 2; ++half) {
@@ -527,9 +528,9 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
         else
             wait_vmem();
         lds_barrier();
-        if (hh + 1 < nh && (NBX == 1 || (NBH == 1 && c > 0))) {   // single-buffered tiles
+        if (hh + 1 < nh && (NBX == 1 || (NBH == 1 && hc))) {   // single-buffered tiles
             if (NBX == 1) issue_x(hh + 1, xnext);
-            if (NBH == 1 && c > 0) issue_h(hh + 1, hnext);
+            if (NBH == 1 && hc) issue_h(hh + 1, hnext);
             wait_vmem();
             lds_barrier();
         }

@@ -173,17 +173,25 @@ ssd_status ssd_chunk_cumsum_state(const ssd_dims* d, const void* x, const float*
     return to_status(ssd::launch_chunk_state(p, d->dtype, d->state_dtype, stream));
 }
 
-ssd_status ssd_state_passing(const ssd_dims* d, const float* cs, void* states, float* final_state,
-                             hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+ssd_status state_passing_impl(const ssd_dims* d, const float* cs, void* states, const float* init,
+                              float* final_state, hipStream_t stream) {
     ssd_status st = ssd_check_dims(d);
     if (st != SSD_OK) return st;
     if (!final_state) return SSD_ERR_NULL_POINTER;
-    if (!aligned16(final_state)) return SSD_ERR_MISALIGNED;
+    if (!aligned16(final_state) || (init && !aligned16(init))) return SSD_ERR_MISALIGNED;
     ssd::Params p = make_params(d);
     p.final_state = final_state;
+    p.init_state = init;
     if (d->batch == 0) return SSD_OK;
+    const int64_t nstate = d->batch * d->nheads * d->dstate * d->headdim;
     if (d->seqlen == 0)
-        return to_status(ssd::launch_zero_fill(final_state, d->batch * d->nheads * d->dstate * d->headdim, stream));
+        return init ? to_status(hipMemcpyAsync(final_state, init, (size_t)nstate * sizeof(float),
+                                               hipMemcpyDeviceToDevice, stream))
+                    : to_status(ssd::launch_zero_fill(final_state, nstate, stream));
     if (!cs || !states) return SSD_ERR_NULL_POINTER;
     if (!aligned16(cs) || !aligned16(states)) return SSD_ERR_MISALIGNED;
     p.cs = const_cast<float*>(cs);
@@ -191,9 +199,9 @@ ssd_status ssd_state_passing(const ssd_dims* d, const float* cs, void* states, f
     return to_status(ssd::launch_state_passing(p, d->state_dtype, stream));
 }
 
-ssd_status ssd_chunk_scan(const ssd_dims* d, const void* x, const float* dt, const void* B,
-                          const void* C, const float* D, const float* cs, const void* states,
-                          void* y, hipStream_t stream) {
+ssd_status chunk_scan_impl(const ssd_dims* d, const void* x, const float* dt, const void* B, const void* C,
+                           const float* D, const float* cs, const void* states, int read_h0, void* y,
+                           hipStream_t stream) {
     ssd_status st = ssd_check_dims(d);
     if (st != SSD_OK) return st;
     if (empty(d)) return SSD_OK;
@@ -210,31 +218,71 @@ ssd_status ssd_chunk_scan(const ssd_dims* d, const void* x, const float* dt, con
     p.cs = const_cast<float*>(cs);
     p.states = const_cast<void*>(states);
     p.y = y;
+    p.read_h0 = read_h0;
     return to_status(ssd::launch_chunk_scan(p, d->dtype, d->state_dtype, stream));
+}
+
+ssd_status forward_impl(const ssd_dims* d, const void* x, const float* dt, const float* A, const void* B,
+                        const void* C, const float* D, const float* init, void* y, float* final_state,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    ssd_status st = ssd_check_dims(d);
+    if (st != SSD_OK) return st;
+    if (d->batch == 0) return SSD_OK;
+    if (d->seqlen == 0) return state_passing_impl(d, nullptr, nullptr, init, final_state, stream);
+    if (!final_state) return SSD_ERR_NULL_POINTER;
+    if (!x || !dt || !A || !B || !C || !D || !y || !workspace) return SSD_ERR_NULL_POINTER;
+    if (!aligned16(final_state) || !aligned16(x) || !aligned16(dt) || !aligned16(A) || !aligned16(B) ||
+        !aligned16(C) || !aligned16(D) || !aligned16(y) || !aligned16(workspace) || (init && !aligned16(init)))
+        return SSD_ERR_MISALIGNED;
+    if (workspace_bytes < ssd_workspace_size(d)) return SSD_ERR_WORKSPACE_TOO_SMALL;
+    float* cs = static_cast<float*>(workspace);
+    void* states = static_cast<unsigned char*>(workspace) + round_up(cs_bytes_of(d));
+    st = ssd_chunk_cumsum_state(d, x, dt, A, B, cs, states, stream);
+    if (st == SSD_OK) st = state_passing_impl(d, cs, states, init, final_state, stream);
+    if (st == SSD_OK) st = chunk_scan_impl(d, x, dt, B, C, D, cs, states, init ? 1 : 0, y, stream);
+    return st;
+}
+
+}  // namespace
+
+extern "C" {
+
+ssd_status ssd_state_passing(const ssd_dims* d, const float* cs, void* states, float* final_state,
+                             hipStream_t stream) {
+    return state_passing_impl(d, cs, states, nullptr, final_state, stream);
+}
+
+ssd_status ssd_state_passing_init(const ssd_dims* d, const float* cs, void* states, const float* initial_state,
+                                  float* final_state, hipStream_t stream) {
+    return state_passing_impl(d, cs, states, initial_state, final_state, stream);
+}
+
+ssd_status ssd_chunk_scan(const ssd_dims* d, const void* x, const float* dt, const void* B,
+                          const void* C, const float* D, const float* cs, const void* states,
+                          void* y, hipStream_t stream) {
+    return chunk_scan_impl(d, x, dt, B, C, D, cs, states, 0, y, stream);
+}
+
+ssd_status ssd_chunk_scan_init(const ssd_dims* d, const void* x, const float* dt, const void* B,
+                               const void* C, const float* D, const float* cs, const void* states,
+                               void* y, hipStream_t stream) {
+    return chunk_scan_impl(d, x, dt, B, C, D, cs, states, 1, y, stream);
 }
 
 ssd_status ssd_forward(const ssd_dims* d, const void* x, const float* dt, const float* A,
                        const void* B, const void* C, const float* D, void* y,
                        float* final_state, void* workspace, size_t workspace_bytes,
                        hipStream_t stream) {
-    ssd_status st = ssd_check_dims(d);
-    if (st != SSD_OK) return st;
-    if (d->batch == 0) return SSD_OK;
-    if (!final_state) return SSD_ERR_NULL_POINTER;
-    if (!aligned16(final_state)) return SSD_ERR_MISALIGNED;
-    if (d->seqlen == 0)
-        return to_status(ssd::launch_zero_fill(final_state, d->batch * d->nheads * d->dstate * d->headdim, stream));
-    if (!x || !dt || !A || !B || !C || !D || !y || !workspace) return SSD_ERR_NULL_POINTER;
-    if (!aligned16(x) || !aligned16(dt) || !aligned16(A) || !aligned16(B) || !aligned16(C) ||
-        !aligned16(D) || !aligned16(y) || !aligned16(workspace))
-        return SSD_ERR_MISALIGNED;
-    if (workspace_bytes < ssd_workspace_size(d)) return SSD_ERR_WORKSPACE_TOO_SMALL;
-    float* cs = static_cast<float*>(workspace);
-    void* states = static_cast<unsigned char*>(workspace) + round_up(cs_bytes_of(d));
-    st = ssd_chunk_cumsum_state(d, x, dt, A, B, cs, states, stream);
-    if (st == SSD_OK) st = ssd_state_passing(d, cs, states, final_state, stream);
-    if (st == SSD_OK) st = ssd_chunk_scan(d, x, dt, B, C, D, cs, states, y, stream);
-    return st;
+    return forward_impl(d, x, dt, A, B, C, D, nullptr, y, final_state, workspace, workspace_bytes, stream);
+}
+
+ssd_status ssd_forward_init(const ssd_dims* d, const void* x, const float* dt, const float* A,
+                            const void* B, const void* C, const float* D, const float* initial_state,
+                            void* y, float* final_state, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+    return forward_impl(d, x, dt, A, B, C, D, initial_state, y, final_state, workspace, workspace_bytes,
+                        stream);
 }
 
 }  // extern "C"
+

@@ -42,6 +42,8 @@ struct Params {
     int fuse_cs;        // chunk_state also computes (and writes) cs from dt and A
     void* y;
     float* final_state;
+    const float* init_state;   // state before the first token [b,H,N,P]; nullptr: zero
+    int read_h0;               // chunk_scan applies states[., 0] (h_0) to the first chunk too
 };
 
 // ---- element traits --------------------------------------------------------

@@ -1,9 +1,9 @@
 // ssd_state_passing: the inter-chunk recurrence on chunk states.
 //
 // "Transformers are SSMs" (chapterpal summary), Knowl 2, the sequential loop
-// h_{c+1} = (a_0 ... a_{Q-1} of chunk c) h_c + S_c with h_0 = 0 and
-// h_final = h_{T/Q} (the state-passing / chunkwise mode of appendix B.3.2).
-// The product of a chunk's decays is exp(cs_last).
+// h_{c+1} = (a_0 ... a_{Q-1} of chunk c) h_c + S_c with h_0 = 0 (or a given
+// initial state) and h_final = h_{T/Q} (the state-passing / chunkwise mode of
+// appendix B.3.2). The product of a chunk's decays is exp(cs_last).
 //
 // Every state element follows its own scalar recurrence, so the kernel is a
 // pure stream: each thread owns 8 consecutive elements of one (batch, head)
@@ -72,9 +72,20 @@ __global__ __launch_bounds__(kPassThreads) void ssd_state_passing_kernel(Params 
     const int64_t cstride = H * PN;
     using O = Oct<ST>;
 
+    // the running state starts at h_0: zero, or the given initial state
+    // ([N][P] per head, so element pr * N + n of the transposed state is
+    // init[n * P + pr])
     f32x8 run;
 #pragma unroll
     for (int k = 0; k < 8; ++k) run[k] = 0.0f;
+    if (p.init_state && live) {
+        const float* ini = p.init_state + (b * H + h) * PN;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int64_t i = e + k, pr = i / N, n = i % N;
+            run[k] = ini[n * P + pr];
+        }
+    }
     typename O::raw cur[kPassWin], nxt[kPassWin];
     float acur[kPassWin], anxt[kPassWin];
     auto load_win = [&](typename O::raw (&w)[kPassWin], float (&a)[kPassWin], int64_t c0) {

@@ -125,6 +125,14 @@ def generate_slow_decay(w: Workload, seed: int = 0) -> dict:
     return inp
 
 
+def generate_initial_state(w: Workload, seed: int = 0, scale: float = 1.0) -> torch.Tensor:
+    """A state to start the recurrence from, [b,H,N,P] fp32: N(0,1) * scale
+    (a carried state is a sum of dt-weighted B x^T terms of about this size)."""
+    rng = np.random.default_rng(seed + 104729)
+    s = rng.standard_normal((w.batch, w.nheads, w.dstate, w.headdim)) * scale
+    return torch.from_numpy(s.astype(np.float32))
+
+
 def to_float64(inp: dict) -> dict:
     """Exact upcast of the stored bits to float64 numpy arrays."""
     return {k: v.float().numpy().astype(np.float64) for k, v in inp.items()}

@@ -151,6 +151,29 @@ def test_stage_argument_errors(lib):
     assert lib.ssd_chunk_scan(P(e), None, None, None, None, None, None, None, None, None) == OK
 
 
+def test_initial_state_argument_errors(lib):
+    d = dims()
+    ws = ssd.ssd_workspace_size(d)
+    good = [_fake(0x100000 * (i + 1)) for i in range(11)]
+    x, dt, A, B, C, D, ini, y, fin, work = good[:10]
+    f = lib.ssd_forward_init
+    P = ctypes.byref
+    assert f(P(d), None, dt, A, B, C, D, ini, y, fin, work, ws, None) == NULLP
+    assert f(P(d), x, dt, A, B, C, D, ini, y, None, work, ws, None) == NULLP
+    assert f(P(d), x, dt, A, B, C, D, _fake(0x100004), y, fin, work, ws, None) == MISAL
+    assert f(P(d), x, dt, A, B, C, D, ini, y, fin, work, ws - 1, None) == WS
+    assert f(P(dims(ngroups=3)), x, dt, A, B, C, D, ini, y, fin, work, ws, None) == SHAPE
+    assert f(P(dims(batch=0)), None, None, None, None, None, None, None, None, None, None, 0, None) == OK
+    a = _fake(0x200000)
+    assert lib.ssd_state_passing_init(P(d), a, a, a, None, None) == NULLP
+    assert lib.ssd_state_passing_init(P(d), None, a, a, a, None) == NULLP
+    assert lib.ssd_state_passing_init(P(d), a, a, _fake(0x200004), a, None) == MISAL
+    assert lib.ssd_chunk_scan_init(P(d), a, a, a, a, a, a, a, None, None) == NULLP
+    assert lib.ssd_chunk_scan_init(P(dims(headdim=40)), a, a, a, a, a, a, a, a, None) == UNSUP
+    e = dims(seqlen=0)
+    assert lib.ssd_chunk_scan_init(P(e), None, None, None, None, None, None, None, None, None) == OK
+
+
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(ssd, "LIB_PATH", str(tmp_path / "missing.so"))
     monkeypatch.setattr(ssd, "_lib", None)
