@@ -331,6 +331,34 @@ def main() -> int:
                "tokens_per_s": round(w.batch * w.seqlen / (alt_ms * 1e-3), 1)}
         del ws2
 
+    # the decoding step (ssd_step) at the same layer shape: one token per
+    # sequence, the fp32 state read and written in place
+    dstep = ssd.make_dims(w.batch, 1, w.nheads, w.headdim, w.dstate, w.ngroups, 32, w.dtype, "fp32")
+    sx, sdt = g["x"][:, 0].contiguous(), g["dt"][:, 0].contiguous()
+    sB, sC = g["B"][:, 0].contiguous(), g["C"][:, 0].contiguous()
+    sstate = torch.zeros((w.batch, w.nheads, w.dstate, w.headdim), dtype=torch.float32, device=dev)
+    sy = torch.empty_like(sx)
+    for _ in range(args.warmup):
+        ssd.ssd_step(dstep, sx, sdt, g["A"], sB, sC, g["D"], sstate, sy, sh)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    nstep = 200
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(nstep):
+        ssd.ssd_step(dstep, sx, sdt, g["A"], sB, sC, g["D"], sstate, sy, sh)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    step_us = e0.elapsed_time(e1) * 1e3 / nstep
+    esz = 2 if w.dtype == "bf16" else 4
+    step_bytes = (2 * 4 * w.batch * w.nheads * w.dstate * w.headdim            # state in and out
+                  + 2 * esz * w.batch * w.nheads * w.headdim                   # x, y
+                  + 2 * esz * w.batch * w.ngroups * w.dstate + 4 * w.batch * w.nheads)
+    decode = {"kernel": "ssd_step", "us_per_step": round(step_us, 2),
+              "tokens_per_s": round(w.batch / (step_us * 1e-6), 1),
+              "GB/s": round(step_bytes / (step_us * 1e-6) / 1e9, 1),
+              "hbm_frac": round(step_bytes / (step_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+              "alg_bytes": step_bytes}
+
     work = kernel_work(w, sbytes)
     peak_tf = MFMA_BF16_PEAK_TFS if w.dtype == "bf16" else MFMA_F32_PEAK_TFS
     per_kernel = {}
@@ -361,6 +389,7 @@ def main() -> int:
         "kernels": per_kernel,
         "evented_ms_per_step": round(staged_ms, 5),
         "other_state_storage": alt,
+        "decode": decode,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

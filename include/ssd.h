@@ -128,6 +128,24 @@ ssd_status ssd_forward_init(const ssd_dims* d, const void* x, const float* dt, c
                             hipStream_t stream);
 
 /*
+ * One token of the recurrence, for decoding ("Transformers are SSMs", Knowl 1,
+ * the recurrent form one step at a time: the inference mode with O(N P) state
+ * per head):
+ *   state[b,h] <- exp(dt[b,h] A[h]) state[b,h] + dt[b,h] B[b,g] x[b,h]^T
+ *   y[b,h]      = C[b,g]^T state[b,h] + D[h] x[b,h],   g = h / (H / G)
+ *   x [b,H,P] (d->dtype), dt [b,H] fp32, A [H], B [b,G,N], C [b,G,N] (d->dtype),
+ *   D [H]: inputs; state [b,H,N,P] fp32, updated in place (the layout of
+ *   ssd_forward's final_state, which can be passed straight in); y [b,H,P]
+ *   (d->dtype) out. d->seqlen, d->chunk_size and d->state_dtype are ignored.
+ * All pointers device, caller-owned, 16-byte aligned; y must not overlap the
+ * inputs or the state. Errors: SSD_ERR_NULL_POINTER, SSD_ERR_MISALIGNED,
+ * SSD_ERR_BAD_SHAPE, SSD_ERR_UNSUPPORTED (P or N outside the supported sets),
+ * SSD_ERR_LAUNCH. batch = 0 is a no-op.
+ */
+ssd_status ssd_step(const ssd_dims* d, const void* x, const float* dt, const float* A, const void* B,
+                    const void* C, const float* D, float* state, void* y, hipStream_t stream);
+
+/*
  * Stage 1 (Knowl 2, "intra-chunk cumulative products of A", taken in log
  * space): cs[b,h,c,j] = sum_{s=0..j} dt[b,cQ+s,h] * A[h], an inclusive prefix
  * sum per chunk, so exp(cs) is the cumulative product of a. Positions past the

@@ -76,6 +76,7 @@ def load_library() -> ctypes.CDLL:
     lib.ssd_chunk_scan.restype = st
     lib.ssd_chunk_scan_init.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.ssd_chunk_scan_init.restype = st
+    lib.ssd_step.argtypes, lib.ssd_step.restype = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp], st
     _lib = lib
     return lib
 
@@ -202,6 +203,12 @@ def ssd_chunk_scan(d, x, dt, B, C, D, cs, states, y, stream=None):
                                          _ptr(D), _ptr(cs), _ptr(states), _ptr(y), s))
 
 
+def ssd_step(d, x, dt, A, B, C, D, state, y, stream=None):
+    s = _stream(state.device) if stream is None else stream
+    _check(load_library().ssd_step(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
+                                   _ptr(D), _ptr(state), _ptr(y), s))
+
+
 # ---- allocating helpers -------------------------------------------------------
 
 def _state_torch_dtype(d: SsdDims) -> torch.dtype:
@@ -236,6 +243,21 @@ def forward(x, dt, A, B, C, D, chunk_size: int, state_dtype: str | None = None, 
             raise ValueError(f"initial_state must be float32 {tuple(final.shape)}")
         ssd_forward_init(d, x, dt, A, B, C, D, initial_state, y, final, workspace, workspace.numel())
     return y, final
+
+
+def step(x, dt, A, B, C, D, state):
+    """One decoding step through ssd_step: x [b,H,P], dt [b,H], B/C [b,G,N];
+    state [b,H,N,P] fp32 is updated in place. Returns y [b,H,P]."""
+    b, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    if x.dtype not in _DTYPE_CODE:
+        raise TypeError(f"x must be float32 or bfloat16, got {x.dtype}")
+    if state.dtype != torch.float32 or tuple(state.shape) != (b, H, N, P):
+        raise ValueError(f"state must be float32 {(b, H, N, P)}")
+    d = make_dims(b, 1, H, P, N, G, 32, x.dtype, "fp32")
+    y = torch.empty_like(x)
+    ssd_step(d, x, dt, A, B, C, D, state, y)
+    return y
 
 
 def stages(x, dt, A, B, C, D, chunk_size: int, state_dtype: str = "fp32"):

@@ -27,7 +27,8 @@ FLAGS = [
     "-Wall", "-Wno-unused-command-line-argument",
     "-I", os.path.join(ROOT, "include"),
 ]
-SOURCES = ["ssd_api.hip", "chunk_cumsum.hip", "chunk_state.hip", "state_passing.hip", "chunk_scan.hip"]
+SOURCES = ["ssd_api.hip", "chunk_cumsum.hip", "chunk_state.hip", "state_passing.hip", "chunk_scan.hip",
+           "ssd_step.hip"]
 
 
 def _compile(src: str) -> str:

@@ -13,6 +13,7 @@ hipError_t launch_chunk_state(const Params& p, int dtype, int state_dtype, hipSt
 hipError_t launch_state_passing(const Params& p, int state_dtype, hipStream_t s);
 hipError_t launch_chunk_scan(const Params& p, int dtype, int state_dtype, hipStream_t s);
 hipError_t launch_zero_fill(float* dst, int64_t n, hipStream_t s);
+hipError_t launch_step(const Params& p, int dtype, hipStream_t s);
 
 // Compute units of the current device (cached per device; 256 if unknown).
 int device_cus();

@@ -276,6 +276,39 @@ ssd_status ssd_forward(const ssd_dims* d, const void* x, const float* dt, const 
     return forward_impl(d, x, dt, A, B, C, D, nullptr, y, final_state, workspace, workspace_bytes, stream);
 }
 
+ssd_status ssd_step(const ssd_dims* d, const void* x, const float* dt, const float* A, const void* B,
+                    const void* C, const float* D, float* state, void* y, hipStream_t stream) {
+    // one token: only the shapes and the input type matter (seqlen, chunk_size
+    // and state_dtype are ignored)
+    static const int64_t kP[] = {16, 32, 64, 128};
+    static const int64_t kN[] = {16, 32, 64, 128, 256};
+    if (!d) return SSD_ERR_NULL_POINTER;
+    if (d->batch < 0 || d->nheads <= 0 || d->headdim <= 0 || d->dstate <= 0 || d->ngroups <= 0 ||
+        d->nheads % d->ngroups != 0)
+        return SSD_ERR_BAD_SHAPE;
+    if (!in_list(d->headdim, kP, 4) || !in_list(d->dstate, kN, 5)) return SSD_ERR_UNSUPPORTED;
+    if (d->dtype != SSD_F32 && d->dtype != SSD_BF16) return SSD_ERR_UNSUPPORTED;
+    if (d->nheads > 0x7FFFFFFF || d->batch > 65535) return SSD_ERR_UNSUPPORTED;
+    if (d->batch == 0) return SSD_OK;
+    ssd_dims one = *d;
+    one.seqlen = 1;
+    one.chunk_size = 32;
+    if (!x || !dt || !A || !B || !C || !D || !state || !y) return SSD_ERR_NULL_POINTER;
+    if (!aligned16(x) || !aligned16(dt) || !aligned16(A) || !aligned16(B) || !aligned16(C) || !aligned16(D) ||
+        !aligned16(state) || !aligned16(y))
+        return SSD_ERR_MISALIGNED;
+    ssd::Params p = make_params(&one);
+    p.x = x;
+    p.dt = dt;
+    p.A = A;
+    p.B = B;
+    p.C = C;
+    p.D = D;
+    p.final_state = state;
+    p.y = y;
+    return to_status(ssd::launch_step(p, d->dtype, stream));
+}
+
 ssd_status ssd_forward_init(const ssd_dims* d, const void* x, const float* dt, const float* A,
                             const void* B, const void* C, const float* D, const float* initial_state,
                             void* y, float* final_state, void* workspace, size_t workspace_bytes,

@@ -174,6 +174,21 @@ def test_initial_state_argument_errors(lib):
     assert lib.ssd_chunk_scan_init(P(e), None, None, None, None, None, None, None, None, None) == OK
 
 
+def test_step_argument_errors(lib):
+    P = ctypes.byref
+    a = _fake(0x300000)
+    d = dims()
+    assert lib.ssd_step(None, a, a, a, a, a, a, a, a, None) == NULLP
+    assert lib.ssd_step(P(d), None, a, a, a, a, a, a, a, None) == NULLP
+    assert lib.ssd_step(P(d), a, a, a, a, a, a, None, a, None) == NULLP
+    assert lib.ssd_step(P(d), a, a, a, a, a, a, _fake(0x300008), a, None) == MISAL
+    assert lib.ssd_step(P(dims(headdim=40)), a, a, a, a, a, a, a, a, None) == UNSUP
+    assert lib.ssd_step(P(dims(ngroups=3)), a, a, a, a, a, a, a, a, None) == SHAPE
+    # the sequence length and chunk size play no part in one step
+    assert lib.ssd_step(P(dims(batch=0, seqlen=0, chunk_size=7)), None, None, None, None, None, None,
+                        None, None, None) == OK
+
+
 def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(ssd, "LIB_PATH", str(tmp_path / "missing.so"))
     monkeypatch.setattr(ssd, "_lib", None)
