@@ -331,6 +331,24 @@ def main() -> int:
                "tokens_per_s": round(w.batch * w.seqlen / (alt_ms * 1e-3), 1)}
         del ws2
 
+    # the forward with the output gate y * silu(z) fused (ssd_forward_gated)
+    zg = inputs.generate_gate(w, seed=1).to(dev)
+    yg = torch.empty_like(g["x"])
+
+    def gated():
+        ssd.ssd_forward_gated(d, g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], None, zg, yg, final, ws,
+                              ws.numel(), sh)
+
+    for _ in range(args.warmup):
+        gated()
+    torch.cuda.synchronize()
+    tg = time.perf_counter()
+    for _ in range(args.steps):
+        gated()
+    torch.cuda.synchronize()
+    gated_ms = (time.perf_counter() - tg) * 1e3 / args.steps
+    del zg, yg
+
     # the decoding step (ssd_step) at the same layer shape: one token per
     # sequence, the fp32 state read and written in place
     dstep = ssd.make_dims(w.batch, 1, w.nheads, w.headdim, w.dstate, w.ngroups, 32, w.dtype, "fp32")
@@ -389,6 +407,8 @@ def main() -> int:
         "kernels": per_kernel,
         "evented_ms_per_step": round(staged_ms, 5),
         "other_state_storage": alt,
+        "gated": {"entry": "ssd_forward_gated", "ms_per_step": round(gated_ms, 5),
+                  "tokens_per_s": round(w.batch * w.seqlen / (gated_ms * 1e-3), 1)},
         "decode": decode,
         "cpu_baseline": None,
     }

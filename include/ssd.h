@@ -128,6 +128,21 @@ ssd_status ssd_forward_init(const ssd_dims* d, const void* x, const float* dt, c
                             hipStream_t stream);
 
 /*
+ * Full forward with the output gate of the Mamba-2 block fused into the chunk
+ * scan's epilogue ("Transformers are SSMs", Knowl 6: the SSD output is gated
+ * by SiLU of the block's z branch before the norm and the output projection):
+ *   y = SSD(x, dt, A, B, C, D; initial_state) * silu(z),  silu(z) = z / (1 + e^{-z})
+ * elementwise, z [b,T,H,P] in d->dtype (device, caller-owned, 16-byte aligned,
+ * read only, required when b > 0 and T > 0). final_state is the ungated
+ * state; initial_state as for ssd_forward_init (NULL: zero). Other arguments
+ * and errors as ssd_forward_init.
+ */
+ssd_status ssd_forward_gated(const ssd_dims* d, const void* x, const float* dt, const float* A,
+                             const void* B, const void* C, const float* D, const float* initial_state,
+                             const void* z, void* y, float* final_state, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+
+/*
  * One token of the recurrence, for decoding ("Transformers are SSMs", Knowl 1,
  * the recurrent form one step at a time: the inference mode with O(N P) state
  * per head):

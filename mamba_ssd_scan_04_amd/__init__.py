@@ -66,6 +66,8 @@ def load_library() -> ctypes.CDLL:
     lib.ssd_forward.restype = st
     lib.ssd_forward_init.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.ssd_forward_init.restype = st
+    lib.ssd_forward_gated.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.ssd_forward_gated.restype = st
     lib.ssd_chunk_cumsum.argtypes, lib.ssd_chunk_cumsum.restype = [P, vp, vp, vp, vp], st
     lib.ssd_chunk_state.argtypes, lib.ssd_chunk_state.restype = [P, vp, vp, vp, vp, vp, vp], st
     lib.ssd_chunk_cumsum_state.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
@@ -162,6 +164,14 @@ def ssd_forward_init(d, x, dt, A, B, C, D, initial_state, y, final_state, worksp
                                            _ptr(final_state), _ptr(workspace), workspace_bytes, s))
 
 
+def ssd_forward_gated(d, x, dt, A, B, C, D, initial_state, z, y, final_state, workspace, workspace_bytes,
+                      stream=None):
+    s = _stream(final_state.device) if stream is None else stream
+    _check(load_library().ssd_forward_gated(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
+                                            _ptr(C), _ptr(D), _ptr(initial_state), _ptr(z), _ptr(y),
+                                            _ptr(final_state), _ptr(workspace), workspace_bytes, s))
+
+
 def ssd_chunk_cumsum(d, dt, A, cs, stream=None):
     s = _stream(dt.device) if stream is None else stream
     _check(load_library().ssd_chunk_cumsum(ctypes.byref(d), _ptr(dt), _ptr(A), _ptr(cs), s))
@@ -221,9 +231,11 @@ def alloc_workspace(d: SsdDims, device) -> torch.Tensor:
 
 
 def forward(x, dt, A, B, C, D, chunk_size: int, state_dtype: str | None = None, workspace=None,
-            initial_state=None):
+            initial_state=None, z=None):
     """y, final_state = SSD(x, dt, A, B, C, D) through ssd_forward (or
-    ssd_forward_init when initial_state [b,H,N,P] fp32 is given).
+    ssd_forward_init when initial_state [b,H,N,P] fp32 is given, or
+    ssd_forward_gated, y * silu(z), when the gate input z (x's shape and
+    type) is given).
 
     state_dtype is the storage of the inter-chunk states in the workspace
     ("fp32" or "bf16"; default: that of x). The running state and the returned
@@ -236,7 +248,14 @@ def forward(x, dt, A, B, C, D, chunk_size: int, state_dtype: str | None = None, 
     final = torch.empty((d.batch, d.nheads, d.dstate, d.headdim), dtype=torch.float32, device=x.device)
     if workspace is None:
         workspace = alloc_workspace(d, x.device)
-    if initial_state is None:
+    if initial_state is not None and (initial_state.dtype != torch.float32
+                                      or tuple(initial_state.shape) != tuple(final.shape)):
+        raise ValueError(f"initial_state must be float32 {tuple(final.shape)}")
+    if z is not None:
+        if z.dtype != x.dtype or z.shape != x.shape:
+            raise ValueError("z must have x's shape and type")
+        ssd_forward_gated(d, x, dt, A, B, C, D, initial_state, z, y, final, workspace, workspace.numel())
+    elif initial_state is None:
         ssd_forward(d, x, dt, A, B, C, D, y, final, workspace, workspace.numel())
     else:
         if initial_state.dtype != torch.float32 or tuple(initial_state.shape) != tuple(final.shape):

@@ -30,8 +30,10 @@
 //  "fragment order", and the x fragment is read from LDS with transpose reads
 //  in the same order. The products are formed transposed (Y^T = X^T M^T), so
 //  each lane ends with 16 values of p for one token j. The carried-state term
-//  is (C . h_c) with rows scaled by exp(cs_j). The epilogue adds D x_j and
-//  stores y in 16-byte pieces of token rows.
+//  is (C . h_c) with rows scaled by exp(cs_j). The epilogue adds D x_j,
+//  optionally multiplies by the gate silu(z) (the Mamba-2 block's output gate,
+//  "Transformers are SSMs", Knowl 6) and stores y in 16-byte pieces of token
+//  rows.
 #include "kernels.hpp"
 
 namespace ssd {
@@ -72,7 +74,9 @@ __device__ __forceinline__ typename Vec8<T>::type x_frag(const unsigned char* xt
     }
 }
 
-template <typename T, int PT, int NT, typename ST, int NBX, int NBH, bool CBL>
+// GATE: y *= silu(z) in the epilogue (a separate instantiation, so that the
+// plain kernel carries none of its registers)
+template <typename T, int PT, int NT, typename ST, int NBX, int NBH, bool CBL, bool GATE>
 __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, int hpw) {
     using Cfg = ScanCfg<T, PT, NT, ST>;
     using V8 = typename Vec8<T>::type;
@@ -339,6 +343,26 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt) acc[pt] = zero16();
             const float c2j = c2v[jl];
+            // gate inputs of this lane's outputs (token jl, the 4 p of each
+            // accumulator quarter), loaded now and used in the epilogue
+            typedef __attribute__((ext_vector_type(4))) T T4;
+            T4 zq[PT][GATE ? 4 : 1];
+            if constexpr (GATE) {
+                const T* zr = static_cast<const T*>(p.z) +
+                              ((tok0 + min(jl, qch - 1)) * H + h0 + (int64_t)hh * hs) * P;
+#pragma unroll
+                for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+                    for (int gq = 0; gq < 4; ++gq) {
+                        const int p0 = min(pt * 32 + 8 * gq + 4 * hf, (int)P - 4);
+                        zq[pt][gq] = *(const __attribute__((address_space(1))) T4*)(zr + p0);
+                    }
+            }
+            // y * silu(z) = y z / (1 + exp(-z))
+            auto gate = [&](float yv, T zv) {
+                const float zf = to_f32(zv);
+                return yv * (zf / (1.0f + __expf(-zf)));
+            };
             const float ej = ecs[jl];
 
             // stage k < rt: off-diagonal key tile k; k == rt: the diagonal tile.
@@ -473,7 +497,11 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
                             const bf16x4 xv = *reinterpret_cast<const bf16x4*>(xt + xo);
                             bf16x4 yv;
 #pragma unroll
-                            for (int r = 0; r < 4; ++r) yv[r] = from_f32<T>(acc[pt][4 * gq + r] + Dh * to_f32(xv[r]));
+                            for (int r = 0; r < 4; ++r) {
+                                const float v = acc[pt][4 * gq + r] + Dh * to_f32(xv[r]);
+                                if constexpr (GATE) yv[r] = from_f32<T>(gate(v, zq[pt][gq][r]));
+                                else yv[r] = from_f32<T>(v);
+                            }
                             const u32x2 wv = __builtin_bit_cast(u32x2, yv);
                             w[q][0] = wv[0];
                             w[q][1] = wv[1];
@@ -500,7 +528,11 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
                         const f32x4 xv = *reinterpret_cast<const f32x4*>(xt + xo);
                         f32x4 yv;
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) yv[r] = acc[pt][4 * gq + r] + Dh * xv[r];
+                        for (int r = 0; r < 4; ++r) {
+                            const float v = acc[pt][4 * gq + r] + Dh * xv[r];
+                            if constexpr (GATE) yv[r] = gate(v, zq[pt][gq][r]);
+                            else yv[r] = v;
+                        }
                         if (jok && p0 < (int)P)
                             *(__attribute__((address_space(1))) f32x4*)(yh + (uint32_t)jl * ystride + p0 * ESZ) = yv;
                         else
@@ -539,7 +571,8 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
 
 template <typename T, int PT, int NT, typename ST, int NBX, int NBH, bool CBL>
 static hipError_t launch_sc2(const Params& p, int hpw, int lds, hipStream_t s) {
-    auto kern = ssd_chunk_scan_kernel<T, PT, NT, ST, NBX, NBH, CBL>;
+    auto kern = p.z ? ssd_chunk_scan_kernel<T, PT, NT, ST, NBX, NBH, CBL, true>
+                    : ssd_chunk_scan_kernel<T, PT, NT, ST, NBX, NBH, CBL, false>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;

@@ -200,8 +200,8 @@ ssd_status state_passing_impl(const ssd_dims* d, const float* cs, void* states, 
 }
 
 ssd_status chunk_scan_impl(const ssd_dims* d, const void* x, const float* dt, const void* B, const void* C,
-                           const float* D, const float* cs, const void* states, int read_h0, void* y,
-                           hipStream_t stream) {
+                           const float* D, const float* cs, const void* states, int read_h0, const void* z,
+                           void* y, hipStream_t stream) {
     ssd_status st = ssd_check_dims(d);
     if (st != SSD_OK) return st;
     if (empty(d)) return SSD_OK;
@@ -219,12 +219,14 @@ ssd_status chunk_scan_impl(const ssd_dims* d, const void* x, const float* dt, co
     p.states = const_cast<void*>(states);
     p.y = y;
     p.read_h0 = read_h0;
+    if (z && !aligned16(z)) return SSD_ERR_MISALIGNED;
+    p.z = z;
     return to_status(ssd::launch_chunk_scan(p, d->dtype, d->state_dtype, stream));
 }
 
 ssd_status forward_impl(const ssd_dims* d, const void* x, const float* dt, const float* A, const void* B,
-                        const void* C, const float* D, const float* init, void* y, float* final_state,
-                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                        const void* C, const float* D, const float* init, const void* z, void* y,
+                        float* final_state, void* workspace, size_t workspace_bytes, hipStream_t stream) {
     ssd_status st = ssd_check_dims(d);
     if (st != SSD_OK) return st;
     if (d->batch == 0) return SSD_OK;
@@ -232,14 +234,15 @@ ssd_status forward_impl(const ssd_dims* d, const void* x, const float* dt, const
     if (!final_state) return SSD_ERR_NULL_POINTER;
     if (!x || !dt || !A || !B || !C || !D || !y || !workspace) return SSD_ERR_NULL_POINTER;
     if (!aligned16(final_state) || !aligned16(x) || !aligned16(dt) || !aligned16(A) || !aligned16(B) ||
-        !aligned16(C) || !aligned16(D) || !aligned16(y) || !aligned16(workspace) || (init && !aligned16(init)))
+        !aligned16(C) || !aligned16(D) || !aligned16(y) || !aligned16(workspace) || (init && !aligned16(init)) ||
+        (z && !aligned16(z)))
         return SSD_ERR_MISALIGNED;
     if (workspace_bytes < ssd_workspace_size(d)) return SSD_ERR_WORKSPACE_TOO_SMALL;
     float* cs = static_cast<float*>(workspace);
     void* states = static_cast<unsigned char*>(workspace) + round_up(cs_bytes_of(d));
     st = ssd_chunk_cumsum_state(d, x, dt, A, B, cs, states, stream);
     if (st == SSD_OK) st = state_passing_impl(d, cs, states, init, final_state, stream);
-    if (st == SSD_OK) st = chunk_scan_impl(d, x, dt, B, C, D, cs, states, init ? 1 : 0, y, stream);
+    if (st == SSD_OK) st = chunk_scan_impl(d, x, dt, B, C, D, cs, states, init ? 1 : 0, z, y, stream);
     return st;
 }
 
@@ -260,20 +263,20 @@ ssd_status ssd_state_passing_init(const ssd_dims* d, const float* cs, void* stat
 ssd_status ssd_chunk_scan(const ssd_dims* d, const void* x, const float* dt, const void* B,
                           const void* C, const float* D, const float* cs, const void* states,
                           void* y, hipStream_t stream) {
-    return chunk_scan_impl(d, x, dt, B, C, D, cs, states, 0, y, stream);
+    return chunk_scan_impl(d, x, dt, B, C, D, cs, states, 0, nullptr, y, stream);
 }
 
 ssd_status ssd_chunk_scan_init(const ssd_dims* d, const void* x, const float* dt, const void* B,
                                const void* C, const float* D, const float* cs, const void* states,
                                void* y, hipStream_t stream) {
-    return chunk_scan_impl(d, x, dt, B, C, D, cs, states, 1, y, stream);
+    return chunk_scan_impl(d, x, dt, B, C, D, cs, states, 1, nullptr, y, stream);
 }
 
 ssd_status ssd_forward(const ssd_dims* d, const void* x, const float* dt, const float* A,
                        const void* B, const void* C, const float* D, void* y,
                        float* final_state, void* workspace, size_t workspace_bytes,
                        hipStream_t stream) {
-    return forward_impl(d, x, dt, A, B, C, D, nullptr, y, final_state, workspace, workspace_bytes, stream);
+    return forward_impl(d, x, dt, A, B, C, D, nullptr, nullptr, y, final_state, workspace, workspace_bytes, stream);
 }
 
 ssd_status ssd_step(const ssd_dims* d, const void* x, const float* dt, const float* A, const void* B,
@@ -313,7 +316,16 @@ ssd_status ssd_forward_init(const ssd_dims* d, const void* x, const float* dt, c
                             const void* B, const void* C, const float* D, const float* initial_state,
                             void* y, float* final_state, void* workspace, size_t workspace_bytes,
                             hipStream_t stream) {
-    return forward_impl(d, x, dt, A, B, C, D, initial_state, y, final_state, workspace, workspace_bytes,
+    return forward_impl(d, x, dt, A, B, C, D, initial_state, nullptr, y, final_state, workspace,
+                        workspace_bytes, stream);
+}
+
+ssd_status ssd_forward_gated(const ssd_dims* d, const void* x, const float* dt, const float* A,
+                             const void* B, const void* C, const float* D, const float* initial_state,
+                             const void* z, void* y, float* final_state, void* workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+    if (d && d->batch > 0 && d->seqlen > 0 && !z) return SSD_ERR_NULL_POINTER;
+    return forward_impl(d, x, dt, A, B, C, D, initial_state, z, y, final_state, workspace, workspace_bytes,
                         stream);
 }
 

@@ -44,6 +44,7 @@ struct Params {
     float* final_state;
     const float* init_state;   // state before the first token [b,H,N,P]; nullptr: zero
     int read_h0;               // chunk_scan applies states[., 0] (h_0) to the first chunk too
+    const void* z;             // gate input [b,T,H,P] (x's type): y *= silu(z); nullptr: no gate
 };
 
 // ---- element traits --------------------------------------------------------

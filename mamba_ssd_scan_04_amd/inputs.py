@@ -133,6 +133,13 @@ def generate_initial_state(w: Workload, seed: int = 0, scale: float = 1.0) -> to
     return torch.from_numpy(s.astype(np.float32))
 
 
+def generate_gate(w: Workload, seed: int = 0) -> torch.Tensor:
+    """The gate branch z [b,T,H,P] for a fused y * silu(z): N(0,1) in x's type."""
+    rng = np.random.default_rng(seed + 130363)
+    z = rng.standard_normal((w.batch, w.seqlen, w.nheads, w.headdim)).astype(np.float32)
+    return torch.from_numpy(z).to(torch_dtype(w.dtype))
+
+
 def to_float64(inp: dict) -> dict:
     """Exact upcast of the stored bits to float64 numpy arrays."""
     return {k: v.float().numpy().astype(np.float64) for k, v in inp.items()}

@@ -196,6 +196,16 @@ def chunked(x, dt, A, B, C, D, Q: int, init=None):
     return {"y": y, "final": state, "cs": cs_out, "S": S, "h_in": h_in}
 
 
+def silu_gate(y, z):
+    """The Mamba-2 block's output gate ("Transformers are SSMs", Knowl 6, the
+    SiLU(z) branch applied to the SSD output), fp64: y * silu(z) with
+    silu(z) = z / (1 + exp(-z)), elementwise."""
+    y = np.asarray(y, dtype=np.float64)
+    z = np.asarray(z, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return y * (z / (1.0 + np.exp(-z)))
+
+
 def rel_err(got, ref) -> float:
     """max |got - ref| / max |ref| (0 when both are all zero)."""
     got = np.asarray(got, dtype=np.float64)

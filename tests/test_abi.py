@@ -174,6 +174,19 @@ def test_initial_state_argument_errors(lib):
     assert lib.ssd_chunk_scan_init(P(e), None, None, None, None, None, None, None, None, None) == OK
 
 
+def test_gated_forward_argument_errors(lib):
+    d = dims()
+    ws = ssd.ssd_workspace_size(d)
+    good = [_fake(0x400000 * (i + 1)) for i in range(11)]
+    x, dt, A, B, C, D, z, y, fin, work = good[:10]
+    f = lib.ssd_forward_gated
+    P = ctypes.byref
+    assert f(P(d), x, dt, A, B, C, D, None, None, y, fin, work, ws, None) == NULLP    # z required
+    assert f(P(d), x, dt, A, B, C, D, None, _fake(0x400002), y, fin, work, ws, None) == MISAL
+    assert f(P(d), x, dt, A, B, C, D, None, z, y, fin, work, ws - 1, None) == WS
+    assert f(P(dims(batch=0)), None, None, None, None, None, None, None, None, None, None, None, 0, None) == OK
+
+
 def test_step_argument_errors(lib):
     P = ctypes.byref
     a = _fake(0x300000)

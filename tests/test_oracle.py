@@ -333,6 +333,24 @@ def test_initial_state_with_empty_sequence(oracle_mod):
     np.testing.assert_array_equal(fin, init)
 
 
+# ---- output gate (Knowl 6: y * SiLU(z))
+
+def test_silu_gate_identities(oracle_mod):
+    """silu(z) = z sigma(z): pinned by sigma(z) + sigma(-z) = 1, i.e.
+    silu(z) - silu(-z) = z, by the tanh form z (1 + tanh(z/2)) / 2 (a library
+    routine other than exp), and by its limits; the gate is a plain product."""
+    z = np.linspace(-30.0, 30.0, 601)
+    one = np.ones_like(z)
+    s = oracle_mod.silu_gate(one, z)
+    np.testing.assert_allclose(s - oracle_mod.silu_gate(one, -z), z, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(s, z * (1.0 + np.tanh(z / 2.0)) / 2.0, rtol=1e-12, atol=1e-12)
+    assert oracle_mod.silu_gate(1.0, 0.0) == 0.0
+    assert abs(oracle_mod.silu_gate(1.0, -800.0)) == 0.0
+    assert oracle_mod.silu_gate(1.0, 800.0) == 800.0
+    y = np.random.default_rng(25).standard_normal(601)
+    np.testing.assert_allclose(oracle_mod.silu_gate(y, z), y * s, rtol=1e-15, atol=0)
+
+
 MUTANTS = {
     "dropped_skip": ("yt[p] = Dh * xt[p];", "yt[p] = 0.0;"),
     "dropped_dt_input": ("const double u = dtv * Bt[n];", "const double u = Bt[n];"),
