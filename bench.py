@@ -180,8 +180,16 @@ def record_traffic(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, workload,
             return "fp32"
         return None
 
+    def gated(name):
+        """The chunk scan's instantiation with the fused output gate (its last
+        template argument): not what ssd_forward runs."""
+        m = re.search(r"Lb[01]ELb([01])EEEv", name)
+        if m is not None:
+            return m.group(1) == "1"
+        return bool(re.search(r"\btrue>\(ssd::Params", name))
+
     for kern in KERNELS:
-        names = [k for k in fe if kern + "_kernel" in k]
+        names = [k for k in fe if kern + "_kernel" in k and not (kern == "ssd_chunk_scan" and gated(k))]
         if kern != "ssd_chunk_cumsum":
             names = [k for k in names if state_of(k) == state_dtype]
         if len(names) != 1 or names[0] not in wr:

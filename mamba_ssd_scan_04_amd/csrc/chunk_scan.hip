@@ -358,10 +358,11 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
                         zq[pt][gq] = *(const __attribute__((address_space(1))) T4*)(zr + p0);
                     }
             }
-            // y * silu(z) = y z / (1 + exp(-z))
+            // y * silu(z) = y z / (1 + 2^(-z log2 e)), with the hardware exp2 and
+            // reciprocal (z -> -inf gives z * rcp(inf) = -0, z -> +inf gives z)
             auto gate = [&](float yv, T zv) {
                 const float zf = to_f32(zv);
-                return yv * (zf / (1.0f + __expf(-zf)));
+                return yv * (zf * __builtin_amdgcn_rcpf(1.0f + fast_exp2(-zf * kLog2e)));
             };
             const float ej = ecs[jl];
 
