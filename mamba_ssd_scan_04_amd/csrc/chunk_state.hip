@@ -14,9 +14,10 @@
 // k-major operand.
 //
 // Work split. One workgroup (4 wavefronts) takes one chunk and up to HPW heads
-// of one group, which share B. The chunk is consumed in blocks of 32 tokens,
-// double-buffered in LDS: while the matrix cores work on block k, the copy
-// engine path (global_load_lds, no registers) fills block k+1. B and x blocks
+// of one group, which share B. The chunk is consumed in blocks of 32 tokens
+// through a ring of NBUF LDS buffers: while the matrix cores work on block k,
+// buffer loads straight to LDS (no registers) fill blocks k+1 .. k+NBUF-1, and
+// the barrier between blocks does not drain them (lds_barrier). B and x blocks
 // stay token-major in LDS (swizzled rows); the token-contiguous operand
 // fragments come out of LDS transpose reads, and w is applied to the x
 // fragment in registers. Each wavefront owns one head and PT/WPH of its
