@@ -9,6 +9,13 @@ over one batch of seeded synthetic input already resident in HBM; its wall
 clock gives tokens/s. Each kernel's average duration is measured in a second
 timed loop that makes the same launches through the stage entry points with
 HIP events between them on the launch stream. Rank 0 prints one JSON line.
+
+Beside the headline figures the line carries: per-call medians of the
+forward with warm caches and with a 512 MB scrub written between calls (cold
+last-level cache); the path's bytes against the HBM peak, both the method's
+compulsory bytes and the four-kernel design's; the attainable peaks of a bare
+MFMA loop and a bare streaming copy on this chip; the other storage type of
+the inter-chunk states; the gated forward; and the decoding step.
 """
 from __future__ import annotations
 
@@ -55,6 +62,74 @@ def kernel_work(w, state_bytes: int) -> dict:
                            "flops": int(b * nc * (G * N * Qc * (Qc + 1) + H * P * Qc * (Qc + 1))
                                         + 2 * b * (T - Q) * H * N * P)},
     }
+
+
+def method_bytes(w) -> int:
+    """The bytes the method itself must move with the states kept on chip:
+    x, B, C in and y out, dt in, and the final state out."""
+    e = 2 if w.dtype == "bf16" else 4
+    b, T, H, P, N, G = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups
+    return e * b * T * (2 * H * P + 2 * G * N) + 4 * b * T * H + 4 * b * H * N * P
+
+
+def attainable_peaks(torch, stream) -> dict | None:
+    """What the chip delivers to a bare MFMA loop and to a bare streaming copy
+    (libssd_peak.so), timed with HIP events on the launch stream, beside the
+    datasheet peaks the kernels are reported against."""
+    import ctypes
+
+    path = os.path.join(ROOT, "mamba_ssd_scan_04_amd", "libssd_peak.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.ssd_peak_mfma_bf16.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    lib.ssd_peak_stream.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                    ctypes.c_void_p]
+    sh = ctypes.c_void_p(stream.cuda_stream)
+
+    def timed(fn, reps):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps
+
+    blocks, iters = 2048, 2000
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+
+    def mfma():
+        rc = lib.ssd_peak_mfma_bf16(blocks, iters, ctypes.c_void_p(out.data_ptr()), sh)
+        if rc != 0:
+            raise RuntimeError(f"ssd_peak_mfma_bf16 failed ({rc})")
+
+    t = timed(mfma, 10)
+    mfma_tfs = blocks * 4 * iters * 4 * 32768 / t / 1e12
+    del out
+    nbytes = 1 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+
+    def stream_copy():
+        rc = lib.ssd_peak_stream(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
+                                 nbytes // 16, 16384, sh)
+        if rc != 0:
+            raise RuntimeError(f"ssd_peak_stream failed ({rc})")
+
+    t = timed(stream_copy, 10)
+    stream_gbs = 2 * nbytes / t / 1e9
+    t = timed(lambda: dst.copy_(src), 10)
+    copy_gbs = 2 * nbytes / t / 1e9
+    del src, dst
+    return {"mfma_bf16_TFLOP/s": round(mfma_tfs, 1), "mfma_bf16_frac_of_peak": round(mfma_tfs / MFMA_BF16_PEAK_TFS, 4),
+            "stream_GB/s": round(stream_gbs, 1), "stream_frac_of_peak": round(stream_gbs / HBM_PEAK_GBS, 4),
+            "torch_copy_GB/s": round(copy_gbs, 1),
+            "how": "MFMA: 2048 workgroups x 4 waves x 8000 chained v_mfma_f32_32x32x16_bf16; "
+                   "stream: 1 GiB read + 1 GiB write, 16-byte non-temporal vectors, 16384 workgroups; torch copy_: the same 1 GiB"}
 
 
 def source_sha(kernel: str) -> str:
@@ -307,6 +382,25 @@ def main() -> int:
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
 
+    # per-call event timings, warm and with the caches cold: between calls a
+    # 512 MB scrub buffer (more than the 256 MB last-level cache) is written,
+    # outside the timed interval; medians over the calls
+    scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    per_call = {}
+    for mode in ("warm", "cold"):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for k in range(args.steps):
+            if mode == "cold":
+                scrub.fill_(k & 0xFF)
+            evs[k][0].record(stream)
+            forward()
+            evs[k][1].record(stream)
+        torch.cuda.synchronize()
+        ts = sorted(a.elapsed_time(b) for a, b in evs)
+        per_call[mode] = ts[len(ts) // 2]
+    del scrub
+
     # per-kernel durations: the same launches with events between them
     for _ in range(args.warmup):
         step()
@@ -402,6 +496,14 @@ def main() -> int:
             "unit": "GB/s", "frac": per_kernel[dom]["hbm_frac"], "traffic": traffic}
     tokens = w.batch * w.seqlen
     value = tokens / (ms_per_step * 1e-3)
+    mbytes = method_bytes(w)
+    dbytes = sum(work[n]["bytes"] for n in KERNELS)
+    roof_method = {
+        "method_bytes": mbytes, "method_us_at_peak": round(mbytes / (HBM_PEAK_GBS * 1e9) * 1e6, 2),
+        "method_frac": round(mbytes / (HBM_PEAK_GBS * 1e9) / (ms_per_step * 1e-3), 4),
+        "design_bytes": dbytes, "design_us_at_peak": round(dbytes / (HBM_PEAK_GBS * 1e9) * 1e6, 2),
+        "design_frac": round(dbytes / (HBM_PEAK_GBS * 1e9) / (ms_per_step * 1e-3), 4)}
+    peaks = attainable_peaks(torch, stream)
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
@@ -412,7 +514,11 @@ def main() -> int:
                    "dstate": w.dstate, "ngroups": w.ngroups, "chunk_size": w.chunk_size,
                    "state_dtype": args.state_dtype, "tokens_per_step": tokens},
         "roofline": roof,
+        "path_roofline": roof_method,
         "kernels": per_kernel,
+        "per_call_ms_median": {"warm": round(per_call["warm"], 5), "cold_cache": round(per_call["cold"], 5),
+                               "cold_cache_tokens_per_s": round(tokens / (per_call["cold"] * 1e-3), 1)},
+        "attainable_peaks": peaks,
         "evented_ms_per_step": round(staged_ms, 5),
         "other_state_storage": alt,
         "gated": {"entry": "ssd_forward_gated", "ms_per_step": round(gated_ms, 5),

@@ -3,7 +3,8 @@
     python -m mamba_ssd_scan_04_amd.build
 
 Each .hip file is compiled to an object in parallel, then linked into
-mamba_ssd_scan_04_amd/libssd.so.
+mamba_ssd_scan_04_amd/libssd.so. The attainable-peak probes (an MFMA loop and
+a streaming copy, used by the benchmark only) go into libssd_peak.so.
 """
 from __future__ import annotations
 
@@ -15,6 +16,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libssd.so")
+PEAK_OUT = os.path.join(PKG, "libssd_peak.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 ROOT = os.path.dirname(PKG)
 
@@ -29,6 +31,7 @@ FLAGS = [
 ]
 SOURCES = ["ssd_api.hip", "chunk_cumsum.hip", "chunk_state.hip", "state_passing.hip", "chunk_scan.hip",
            "ssd_step.hip"]
+PEAK_SOURCES = ["peak_probe.hip"]
 
 
 def _compile(src: str) -> str:
@@ -40,18 +43,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = OUT + ".tmp"
+def _link(objs, out: str) -> None:
+    tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + PEAK_SOURCES
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], OUT)
+    _link([objs[s] for s in PEAK_SOURCES], PEAK_OUT)
     if verbose:
-        print(f"built {OUT}")
+        print(f"built {OUT} and {PEAK_OUT}")
     return OUT
 
 

@@ -207,3 +207,20 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(ssd, "_lib", None)
     with pytest.raises(RuntimeError, match="not found"):
         ssd.load_library()
+
+
+def test_peak_probe_library_exports():
+    """The attainable-peak probes the benchmark times (an MFMA loop and a
+    streaming copy) are built beside the SSD library and reject bad
+    arguments before launching anything."""
+    path = os.path.join(os.path.dirname(ssd.LIB_PATH), "libssd_peak.so")
+    if not os.path.exists(path):
+        pytest.skip("libssd_peak.so not built")
+    peak = ctypes.CDLL(path)
+    peak.ssd_peak_mfma_bf16.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    peak.ssd_peak_stream.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                                     ctypes.c_void_p]
+    assert peak.ssd_peak_mfma_bf16(0, 10, _fake(0x1000), None) != 0
+    assert peak.ssd_peak_mfma_bf16(4, 10, None, None) != 0
+    assert peak.ssd_peak_stream(_fake(0x1000), _fake(0x2000), 0, 4, None) != 0
+    assert peak.ssd_peak_stream(_fake(0x1008), _fake(0x2000), 16, 4, None) != 0
