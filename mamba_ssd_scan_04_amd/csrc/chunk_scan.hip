@@ -425,12 +425,15 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
             // keep the compiler from sinking those reads into their uses
             Stage sa, sb;
             if (hc) {   // (h_c^T C^T), then scaled by exp(cs_j)
-                typename Vec8<ST>::type hv[KS / 2][PT];
+                // over n in pieces of at most 4 k16 steps (halves up to N = 128),
+                // each piece's h_c fragments read before its products
+                constexpr int KP = KS / 2 < 4 ? KS / 2 : 4, NPC = KS / KP;
+                typename Vec8<ST>::type hv[KP][PT];
 #pragma unroll
-                for (int half = 0; half < 2; ++half) {
+                for (int half = 0; half < NPC; ++half) {
 #pragma unroll
-                    for (int k2 = 0; k2 < KS / 2; ++k2) {
-                        const int ks = half * (KS / 2) + k2;
+                    for (int k2 = 0; k2 < KP; ++k2) {
+                        const int ks = half * KP + k2;
 #pragma unroll
                         for (int pt = 0; pt < PT; ++pt) {
                             const int cbyte = (ks * 16 + hf * 8) * SSZ;   // 16 or 32 bytes
@@ -445,12 +448,12 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
                             }
                         }
                     }
-                    if (half == 1) load_stage(sa, 0);
+                    if (half == NPC - 1) load_stage(sa, 0);
                     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                    for (int k2 = 0; k2 < KS / 2; ++k2)
+                    for (int k2 = 0; k2 < KP; ++k2)
 #pragma unroll
-                        for (int pt = 0; pt < PT; ++pt) mma_k16(acc[pt], cvt8<T>(hv[k2][pt]), creg[half * (KS / 2) + k2]);
+                        for (int pt = 0; pt < PT; ++pt) mma_k16(acc[pt], cvt8<T>(hv[k2][pt]), creg[half * KP + k2]);
                     __builtin_amdgcn_sched_barrier(0);
                 }
 #pragma unroll
