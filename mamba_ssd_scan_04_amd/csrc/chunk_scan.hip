@@ -425,9 +425,10 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
             // keep the compiler from sinking those reads into their uses
             Stage sa, sb;
             if (hc) {   // (h_c^T C^T), then scaled by exp(cs_j)
-                // over n in pieces of at most 4 k16 steps (halves up to N = 128),
-                // each piece's h_c fragments read before its products
-                constexpr int KP = KS / 2 < 4 ? KS / 2 : 4, NPC = KS / KP;
+                // over n in pieces, each piece's h_c fragments read before its
+                // products: halves up to N = 128; at N = 256, where the wave's
+                // C rows take 64 registers, pieces of 2 k16 steps
+                constexpr int KP = KS <= 8 ? KS / 2 : 2, NPC = KS / KP;
                 typename Vec8<ST>::type hv[KP][PT];
 #pragma unroll
                 for (int half = 0; half < NPC; ++half) {
