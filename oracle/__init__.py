@@ -59,6 +59,10 @@ def _load():
         i64, dp = ctypes.c_int64, ctypes.POINTER(ctypes.c_double)
         lib.ssd_oracle_forward.argtypes = [i64] * 6 + [dp] * 6 + [dp, dp, dp, i64, dp, ctypes.c_int]
         lib.ssd_oracle_forward.restype = ctypes.c_int
+        ip = ctypes.POINTER(ctypes.c_int32)
+        lib.ssd_oracle_forward_varlen.argtypes = ([i64] * 6 + [dp] * 6 + [dp, ip, dp, dp, i64, dp,
+                                                                          ctypes.c_int])
+        lib.ssd_oracle_forward_varlen.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -76,17 +80,25 @@ def default_threads() -> int:
         return os.cpu_count() or 1
 
 
-def recurrence(x, dt, A, B, C, D, snap_every: int = 0, nthreads: int | None = None, init=None):
+def recurrence(x, dt, A, B, C, D, snap_every: int = 0, nthreads: int | None = None, init=None,
+               seq_idx=None):
     """Knowl 1 linear form, fp64. Returns (y, final[, snaps]).
 
     x [b,T,H,P], dt [b,T,H], A [H], B/C [b,T,G,N], D [H] (any float arrays;
     converted to contiguous float64). final is [b,H,N,P]. init [b,H,N,P] is
     the state before the first token (None: zero). With snap_every=Q, also
     returns snaps [b,nc,H,N,P]: the state entering each chunk of Q tokens.
+    seq_idx [b,T] (integer, non-decreasing along T) packs several documents
+    into one row (Knowl 8): the decay is 0 at each token whose id differs from
+    the previous token's, which drops the state entering that document.
     """
     x, dt, A, B, C, D = (np.ascontiguousarray(v, dtype=np.float64) for v in (x, dt, A, B, C, D))
     if init is not None:
         init = np.ascontiguousarray(init, dtype=np.float64)
+    if seq_idx is not None:
+        seq_idx = np.ascontiguousarray(seq_idx, dtype=np.int32)
+        if seq_idx.shape != x.shape[:2]:
+            raise ValueError(f"seq_idx must be [b,T] = {x.shape[:2]}, got {seq_idx.shape}")
     b, T, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
     y = np.empty_like(x)
@@ -97,9 +109,10 @@ def recurrence(x, dt, A, B, C, D, snap_every: int = 0, nthreads: int | None = No
         snaps = np.empty((b, nc, H, N, P))
     if init is not None and init.shape != (b, H, N, P):
         raise ValueError(f"init must be [b,H,N,P] = {(b, H, N, P)}, got {init.shape}")
-    rc = _load().ssd_oracle_forward(b, T, H, P, N, G, _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
-                                    _ptr(C), _ptr(D), _ptr(init), _ptr(y), _ptr(final), snap_every,
-                                    _ptr(snaps), nthreads or default_threads())
+    sp = None if seq_idx is None else seq_idx.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    rc = _load().ssd_oracle_forward_varlen(b, T, H, P, N, G, _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
+                                           _ptr(C), _ptr(D), _ptr(init), sp, _ptr(y), _ptr(final),
+                                           snap_every, _ptr(snaps), nthreads or default_threads())
     if rc != 0:
         raise RuntimeError(f"ssd_oracle_forward failed with code {rc}")
     return (y, final, snaps) if snap_every > 0 else (y, final)
@@ -109,12 +122,13 @@ def _heads_to_groups(H, G):
     return np.arange(H) // (H // G)
 
 
-def quadratic(x, dt, A, B, C, D):
+def quadratic(x, dt, A, B, C, D, seq_idx=None):
     """Knowl 1 dual form by brute force: Y = (L o C B^T) (dt*x) + D x.
 
     L[t, i] is formed as the explicit product a_{i+1} * ... * a_t for t >= i
-    (the empty product, 1, on the diagonal) and 0 above it. O(T^3) per head:
-    for small T only.
+    (the empty product, 1, on the diagonal) and 0 above it. With seq_idx, a_s
+    is 0 at every document start s (Knowl 8). O(T^3) per head: for small T
+    only.
     """
     x, dt, A, B, C, D = (np.asarray(v, dtype=np.float64) for v in (x, dt, A, B, C, D))
     b, T, H, P = x.shape
@@ -124,6 +138,9 @@ def quadratic(x, dt, A, B, C, D):
         for h in range(H):
             g = gid[h]
             a = np.exp(dt[bi, :, h] * A[h])
+            if seq_idx is not None:
+                sq = np.asarray(seq_idx)[bi]
+                a[1:][sq[1:] != sq[:-1]] = 0.0
             Lm = np.zeros((T, T))
             for t in range(T):
                 for i in range(t + 1):

@@ -17,6 +17,13 @@
  *     y[b,t,h,:] = C[b,t,g,:]^T state_t + D[h] * x[b,t,h,:]
  *   final[b,h]   = state_{T-1}
  *
+ * Variable-length packing (Knowl 8: documents concatenated into one sequence,
+ * the state reset at each document start by a zero decay there): with sequence
+ * ids seq [b,T] (int32, non-decreasing along t), the decay
+ * exp(dt[b,t,h] * A[h]) is replaced by 0 at every t > 0 whose id differs from
+ * that of t - 1, so the state entering a document's first token is dropped.
+ * The initial state, if given, enters the first document.
+ *
  * This is the plain definition: the block-decomposition algorithm (Knowl 2)
  * reaches exactly this result, so the oracle is the recurrence itself and not
  * the algorithm. Heads of one group share B and C (Knowl 7, the grouped
@@ -40,6 +47,7 @@
 typedef struct {
     int64_t batch, seqlen, nheads, headdim, dstate, ngroups, every;
     const double *x, *dt, *A, *B, *C, *D, *init;
+    const int32_t* seq;  /* [b,T] sequence ids, or NULL */
     double *y, *final_state, *snaps;
     int64_t next;      /* shared work counter */
     int failed;
@@ -62,7 +70,8 @@ static void run_item(job_t* j, int64_t item, double* st) {
             memcpy(dst, st, sizeof(double) * (size_t)(N * P));
         }
         const double dtv = j->dt[(b * T + t) * H + h];
-        const double a = exp(dtv * Ah);
+        const int starts = j->seq && t > 0 && j->seq[b * T + t] != j->seq[b * T + t - 1];
+        const double a = starts ? 0.0 : exp(dtv * Ah);
         const double* xt = j->x + ((b * T + t) * H + h) * P;
         const double* Bt = j->B + ((b * T + t) * G + g) * N;
         const double* Ct = j->C + ((b * T + t) * G + g) * N;
@@ -101,14 +110,14 @@ static void* worker(void* arg) {
 }
 
 /* Returns 0 on success, -1 on bad arguments, -2 on allocation/thread failure.
- * y and x may not alias. init, final_state and snaps may be NULL (init NULL:
- * zero initial state). every <= 0 turns the snapshots off. nthreads < 1
- * means 1. */
-int ssd_oracle_forward(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
-                       int64_t dstate, int64_t ngroups, const double* x, const double* dt,
-                       const double* A, const double* B, const double* C, const double* D,
-                       const double* init, double* y, double* final_state, int64_t every,
-                       double* snaps, int nthreads) {
+ * y and x may not alias. init, final_state, snaps and seq may be NULL (init
+ * NULL: zero initial state; seq NULL: one sequence per batch row). every <= 0
+ * turns the snapshots off. nthreads < 1 means 1. */
+int ssd_oracle_forward_varlen(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                              int64_t dstate, int64_t ngroups, const double* x, const double* dt,
+                              const double* A, const double* B, const double* C, const double* D,
+                              const double* init, const int32_t* seq, double* y, double* final_state,
+                              int64_t every, double* snaps, int nthreads) {
     if (batch < 0 || seqlen < 0 || nheads <= 0 || headdim <= 0 || dstate <= 0 ||
         ngroups <= 0 || nheads % ngroups != 0)
         return -1;
@@ -126,7 +135,7 @@ int ssd_oracle_forward(int64_t batch, int64_t seqlen, int64_t nheads, int64_t he
     job_t j;
     j.batch = batch; j.seqlen = seqlen; j.nheads = nheads; j.headdim = headdim;
     j.dstate = dstate; j.ngroups = ngroups; j.every = every;
-    j.x = x; j.dt = dt; j.A = A; j.B = B; j.C = C; j.D = D; j.init = init;
+    j.x = x; j.dt = dt; j.A = A; j.B = B; j.C = C; j.D = D; j.init = init; j.seq = seq;
     j.y = y; j.final_state = final_state; j.snaps = (every > 0) ? snaps : NULL;
     j.next = 0; j.failed = 0;
     if (nthreads < 1) nthreads = 1;
@@ -142,4 +151,14 @@ int ssd_oracle_forward(int64_t batch, int64_t seqlen, int64_t nheads, int64_t he
     for (int i = 0; i < started; ++i) pthread_join(th[i], NULL);
     free(th);
     return j.failed ? -2 : 0;
+}
+
+/* The same with one sequence per batch row. */
+int ssd_oracle_forward(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                       int64_t dstate, int64_t ngroups, const double* x, const double* dt,
+                       const double* A, const double* B, const double* C, const double* D,
+                       const double* init, double* y, double* final_state, int64_t every,
+                       double* snaps, int nthreads) {
+    return ssd_oracle_forward_varlen(batch, seqlen, nheads, headdim, dstate, ngroups, x, dt, A, B, C,
+                                     D, init, NULL, y, final_state, every, snaps, nthreads);
 }

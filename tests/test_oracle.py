@@ -335,6 +335,67 @@ def test_initial_state_with_empty_sequence(oracle_mod):
 
 # ---- output gate (Knowl 6: y * SiLU(z))
 
+# ---- variable-length packing ("Transformers are SSMs", Knowl 8: documents
+# concatenated into one row, the state reset by a zero decay at each start)
+
+def _random_seq(rng, b, T, ndocs):
+    """Non-decreasing ids per row with ndocs - 1 random starts in 1 .. T-1,
+    plus a start at t = 1 and two one-token documents at the end."""
+    seq = np.zeros((b, T), dtype=np.int32)
+    for r in range(b):
+        starts = set(rng.choice(np.arange(2, T - 2), size=ndocs - 1, replace=False).tolist())
+        starts |= {1, T - 2, T - 1}
+        seq[r] = np.cumsum([1 if t in starts else 0 for t in range(T)]) + 7 * r
+    return seq
+
+
+def _documents(seq_row):
+    """(start, end) of each document of one row."""
+    cuts = [0] + [t for t in range(1, len(seq_row)) if seq_row[t] != seq_row[t - 1]] + [len(seq_row)]
+    return list(zip(cuts[:-1], cuts[1:]))
+
+
+def test_varlen_matches_bruteforce_dual(oracle_mod):
+    """The recurrence with resets equals the dual form whose mask products
+    take a_s = 0 at every document start (explicit products, no recurrence)."""
+    rng = np.random.default_rng(31)
+    inp = rand_inputs(rng, 2, 24, 3, 3, 4, 1, a_scale=0.1)
+    seq = _random_seq(rng, 2, 24, 4)
+    y, _ = rec(oracle_mod, inp, seq_idx=seq)
+    assert oracle_mod.rel_err(y, oracle_mod.quadratic(**inp, seq_idx=seq)) < 1e-12
+
+
+def test_varlen_documents_are_independent(oracle_mod):
+    """Each packed document gives what it gives alone from a zero state (the
+    first one from the initial state), and the final state is that of the last
+    document run alone."""
+    rng = np.random.default_rng(32)
+    b, T, H, P, N, G = 2, 50, 4, 3, 5, 2
+    inp = rand_inputs(rng, b, T, H, P, N, G, a_scale=0.05)
+    seq = _random_seq(rng, b, T, 5)
+    init = rng.standard_normal((b, H, N, P))
+    for ini in (None, init):
+        y, fin = rec(oracle_mod, inp, seq_idx=seq, init=ini)
+        for r in range(b):
+            row = {k: (v[r:r + 1] if k in ("x", "dt", "B", "C") else v) for k, v in inp.items()}
+            for d, (t0, t1) in enumerate(_documents(seq[r])):
+                start = None if (ini is None or d > 0) else ini[r:r + 1]
+                yd, fd = rec(oracle_mod, _split(row, t0, t1), init=start)
+                assert oracle_mod.rel_err(y[r:r + 1, t0:t1], yd) < 1e-12
+            assert oracle_mod.rel_err(fin[r:r + 1], fd) < 1e-12
+
+
+def test_varlen_one_document_is_the_plain_recurrence(oracle_mod):
+    """A row whose ids never change is one sequence: bit-identical results."""
+    rng = np.random.default_rng(33)
+    inp = rand_inputs(rng, 3, 30, 2, 4, 4, 1)
+    seq = np.repeat(np.array([[5], [0], [-3]], dtype=np.int32), 30, axis=1)
+    y, fin = rec(oracle_mod, inp, seq_idx=seq)
+    y0, fin0 = rec(oracle_mod, inp)
+    np.testing.assert_array_equal(y, y0)
+    np.testing.assert_array_equal(fin, fin0)
+
+
 def test_silu_gate_identities(oracle_mod):
     """silu(z) = z sigma(z): pinned by sigma(z) + sigma(-z) = 1, i.e.
     silu(z) - silu(-z) = z, by the tanh form z (1 + tanh(z/2)) / 2 (a library
@@ -361,6 +422,11 @@ MUTANTS = {
     "stale_state_output": None,
     # the given initial state ignored (zero start)
     "ignored_initial_state": ("    if (j->init)\n        memcpy(st,", "    if (0)\n        memcpy(st,"),
+    # document starts of a packed row not resetting the state
+    "ignored_reset": ("starts ? 0.0 : exp(dtv * Ah)", "exp(dtv * Ah)"),
+    # the reset taken one token late (at the second token of a document)
+    "late_reset": ("const int starts = j->seq && t > 0 && j->seq[b * T + t] != j->seq[b * T + t - 1];",
+                   "const int starts = j->seq && t > 1 && j->seq[b * T + t - 1] != j->seq[b * T + t - 2];"),
 }
 
 UPDATE_BLOCK = """        for (int64_t n = 0; n < N; ++n) {
@@ -402,6 +468,19 @@ def test_planted_mistakes_are_caught(oracle_mod, name):
         lib = ctypes.CDLL(lpath)
         i64, dp = ctypes.c_int64, ctypes.POINTER(ctypes.c_double)
         lib.ssd_oracle_forward.argtypes = [i64] * 6 + [dp] * 6 + [dp, dp, dp, i64, dp, ctypes.c_int]
+        ip = ctypes.POINTER(ctypes.c_int32)
+        lib.ssd_oracle_forward_varlen.argtypes = [i64] * 6 + [dp] * 6 + [dp, ip, dp, dp, i64, dp, ctypes.c_int]
+
+        def run_varlen(inp, seq):
+            x, dt, A, B, C, D = (np.ascontiguousarray(inp[k], dtype=np.float64)
+                                 for k in ("x", "dt", "A", "B", "C", "D"))
+            b, T, H, P = x.shape
+            y = np.empty_like(x)
+            sq = np.ascontiguousarray(seq, dtype=np.int32)
+            pp = lambda a: a.ctypes.data_as(dp)
+            lib.ssd_oracle_forward_varlen(b, T, H, P, B.shape[3], B.shape[2], pp(x), pp(dt), pp(A), pp(B),
+                                          pp(C), pp(D), None, sq.ctypes.data_as(ip), pp(y), None, 0, None, 1)
+            return y
 
         def run(inp, init=None, with_final=False):
             x, dt, A, B, C, D = (np.ascontiguousarray(inp[k], dtype=np.float64)
@@ -427,6 +506,9 @@ def test_planted_mistakes_are_caught(oracle_mod, name):
         _, f1 = run(_split(inp, 0, 5), with_final=True)
         y2 = run(_split(inp, 5, 12), init=f1)
         resume_ok = oracle_mod.rel_err(y2, yfull[:, 5:]) < 1e-12
-        assert not (golden_ok and dual_ok and resume_ok), f"planted mistake {name} was not caught"
+        # packed documents: the brute-force dual form with a = 0 at document starts
+        seq = np.array([[0, 0, 0, 1, 1, 2, 2, 2, 2, 3, 4, 4]], dtype=np.int32)
+        varlen_ok = oracle_mod.rel_err(run_varlen(inp, seq), oracle_mod.quadratic(**inp, seq_idx=seq)) < 1e-12
+        assert not (golden_ok and dual_ok and resume_ok and varlen_ok), f"planted mistake {name} was not caught"
     finally:
         shutil.rmtree(tmp)
