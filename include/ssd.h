@@ -143,6 +143,28 @@ ssd_status ssd_forward_gated(const ssd_dims* d, const void* x, const float* dt, 
                              size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Full forward over rows that pack several documents ("Transformers are SSMs",
+ * Knowl 8: variable-length sequences concatenated, the state reset between
+ * them by a zero decay at each document start). seq_idx [b,T] int32 (device,
+ * caller-owned, read only, 4-byte aligned, required when b > 0 and T > 0)
+ * gives each token's document id; ids must not decrease along T (the values
+ * are not checked; with decreasing ids the result is undefined). At every
+ * t > 0 whose id differs from that of t - 1 the decay exp(dt_t A_h) is taken
+ * as 0, so no state crosses into a new document. initial_state (NULL: zero)
+ * enters the row's first document; final_state is the state after token T - 1,
+ * i.e. that of the last document. Enqueues the chunk-state, state-passing and
+ * chunk-scan kernels in their document-masked instantiations. Errors as
+ * ssd_forward_init, plus SSD_ERR_NULL_POINTER for a missing seq_idx,
+ * SSD_ERR_MISALIGNED for one not 4-byte aligned, and SSD_ERR_UNSUPPORTED when
+ * the chunk scan's LDS has no room for the chunk's ids (4 * chunk_size bytes
+ * beyond the smallest tile set).
+ */
+ssd_status ssd_forward_varlen(const ssd_dims* d, const void* x, const float* dt, const float* A,
+                              const void* B, const void* C, const float* D, const float* initial_state,
+                              const int32_t* seq_idx, void* y, float* final_state, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+
+/*
  * One token of the recurrence, for decoding ("Transformers are SSMs", Knowl 1,
  * the recurrent form one step at a time: the inference mode with O(N P) state
  * per head):

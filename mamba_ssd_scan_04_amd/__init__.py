@@ -68,6 +68,8 @@ def load_library() -> ctypes.CDLL:
     lib.ssd_forward_init.restype = st
     lib.ssd_forward_gated.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.ssd_forward_gated.restype = st
+    lib.ssd_forward_varlen.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.ssd_forward_varlen.restype = st
     lib.ssd_chunk_cumsum.argtypes, lib.ssd_chunk_cumsum.restype = [P, vp, vp, vp, vp], st
     lib.ssd_chunk_state.argtypes, lib.ssd_chunk_state.restype = [P, vp, vp, vp, vp, vp, vp], st
     lib.ssd_chunk_cumsum_state.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
@@ -172,6 +174,14 @@ def ssd_forward_gated(d, x, dt, A, B, C, D, initial_state, z, y, final_state, wo
                                             _ptr(final_state), _ptr(workspace), workspace_bytes, s))
 
 
+def ssd_forward_varlen(d, x, dt, A, B, C, D, initial_state, seq_idx, y, final_state, workspace,
+                       workspace_bytes, stream=None):
+    s = _stream(final_state.device) if stream is None else stream
+    _check(load_library().ssd_forward_varlen(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
+                                             _ptr(C), _ptr(D), _ptr(initial_state), _ptr(seq_idx), _ptr(y),
+                                             _ptr(final_state), _ptr(workspace), workspace_bytes, s))
+
+
 def ssd_chunk_cumsum(d, dt, A, cs, stream=None):
     s = _stream(dt.device) if stream is None else stream
     _check(load_library().ssd_chunk_cumsum(ctypes.byref(d), _ptr(dt), _ptr(A), _ptr(cs), s))
@@ -231,11 +241,12 @@ def alloc_workspace(d: SsdDims, device) -> torch.Tensor:
 
 
 def forward(x, dt, A, B, C, D, chunk_size: int, state_dtype: str | None = None, workspace=None,
-            initial_state=None, z=None):
+            initial_state=None, z=None, seq_idx=None):
     """y, final_state = SSD(x, dt, A, B, C, D) through ssd_forward (or
     ssd_forward_init when initial_state [b,H,N,P] fp32 is given, or
     ssd_forward_gated, y * silu(z), when the gate input z (x's shape and
-    type) is given).
+    type) is given, or ssd_forward_varlen when seq_idx [b,T] int32, the
+    non-decreasing document id of each token, is given; not with z).
 
     state_dtype is the storage of the inter-chunk states in the workspace
     ("fp32" or "bf16"; default: that of x). The running state and the returned
@@ -251,7 +262,14 @@ def forward(x, dt, A, B, C, D, chunk_size: int, state_dtype: str | None = None, 
     if initial_state is not None and (initial_state.dtype != torch.float32
                                       or tuple(initial_state.shape) != tuple(final.shape)):
         raise ValueError(f"initial_state must be float32 {tuple(final.shape)}")
-    if z is not None:
+    if seq_idx is not None:
+        if z is not None:
+            raise ValueError("seq_idx and z together are not supported")
+        if seq_idx.dtype != torch.int32 or tuple(seq_idx.shape) != (d.batch, d.seqlen):
+            raise ValueError(f"seq_idx must be int32 {(d.batch, d.seqlen)}")
+        seq_idx = seq_idx.contiguous()
+        ssd_forward_varlen(d, x, dt, A, B, C, D, initial_state, seq_idx, y, final, workspace, workspace.numel())
+    elif z is not None:
         if z.dtype != x.dtype or z.shape != x.shape:
             raise ValueError("z must have x's shape and type")
         ssd_forward_gated(d, x, dt, A, B, C, D, initial_state, z, y, final, workspace, workspace.numel())

@@ -54,9 +54,10 @@ struct ScanCfg {
     __host__ __device__ static int vbytes(int Q) { return 4 * Q * 4; }
     // the off-diagonal C B^T tiles of all row tiles (kt < rt), when kept in LDS
     __host__ __device__ static int cbbytes(int Q) { return (Q / 32) * (Q / 32 - 1) / 2 * CBTILE; }
-    // bytes of LDS with nbx x buffers, nbh h_c buffers and C B^T in LDS or not
-    __host__ __device__ static int lds(int Q, int nbx, int nbh, bool cbl) {
-        return nbx * xbytes(Q) + nbh * HBYTES + 2 * vbytes(Q) + (cbl ? cbbytes(Q) : 0);
+    // bytes of LDS with nbx x buffers, nbh h_c buffers, C B^T in LDS or not,
+    // and the chunk's document ids (packed documents) or not
+    __host__ __device__ static int lds(int Q, int nbx, int nbh, bool cbl, bool vl = false) {
+        return nbx * xbytes(Q) + nbh * HBYTES + 2 * vbytes(Q) + (cbl ? cbbytes(Q) : 0) + (vl ? 4 * Q : 0);
     }
 };
 
@@ -75,8 +76,12 @@ __device__ __forceinline__ typename Vec8<T>::type x_frag(const unsigned char* xt
 }
 
 // GATE: y *= silu(z) in the epilogue (a separate instantiation, so that the
-// plain kernel carries none of its registers)
-template <typename T, int PT, int NT, typename ST, int NBX, int NBH, bool CBL, bool GATE>
+// plain kernel carries none of its registers). VARLEN: packed documents
+// ("Transformers are SSMs", Knowl 8: the decay is 0 at a document start): the
+// masked product keeps only key tokens of the query's document, and the
+// carried state reaches only rows in the document of the token before the
+// chunk (its own instantiation too).
+template <typename T, int PT, int NT, typename ST, int NBX, int NBH, bool CBL, bool GATE, bool VARLEN>
 __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, int hpw) {
     using Cfg = ScanCfg<T, PT, NT, ST>;
     using V8 = typename Vec8<T>::type;
@@ -88,6 +93,7 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
     unsigned char* const hb0 = smem + NBX * XB;
     float* const vb0 = reinterpret_cast<float*>(hb0 + NBH * Cfg::HBYTES);
     unsigned char* const cbl0 = reinterpret_cast<unsigned char*>(vb0) + 2 * VB;   // C B^T tiles (CBL)
+    int* const sqv = reinterpret_cast<int*>(cbl0 + (CBL ? Cfg::cbbytes(Q) : 0));    // document ids (VARLEN)
 
     // ---- block coordinates (uniform) ----
     const int64_t T_ = p.seqlen, H = p.nheads, P = p.headdim, N = p.dstate, G = p.ngroups;
@@ -147,6 +153,18 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
         dma_tile_issue<NIH>(dst, sbase + (int64_t)hh * hs * P * N * SSZ, offh, wave, kScanWaves);
     };
     float vcs = 0.0f, vcr = 0.0f, vdt = 0.0f;   // thread i holds token i of the next head
+    // packed documents: thread i < Q holds the id of token i (clamped to the
+    // chunk) and whether it is in the document of the token before the chunk
+    // (the first token's for chunk 0, whose carried state is the initial one)
+    int vsq = 0;
+    bool vok = true;
+    if constexpr (VARLEN) {
+        const int* sq = p.seq_idx + b * T_;
+        if ((int)threadIdx.x < Q) {
+            vsq = sq[t0 + min((int)threadIdx.x, qc - 1)];
+            vok = vsq == sq[c > 0 ? t0 - 1 : 0];
+        }
+    }
     auto load_vec = [&](int hh) {
         const int i = threadIdx.x;
         if (i < Q) {
@@ -166,7 +184,7 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
         if (i < Q) {
             const float c2 = vcs * kLog2e, c2r = vcr * kLog2e;
             v[i] = c2;
-            v[Q + i] = exp2f(c2);
+            v[Q + i] = vok ? exp2f(c2) : 0.0f;
             v[2 * Q + i] = exp2f(c2r - c2) * vdt;
             v[3 * Q + i] = vdt;
         }
@@ -297,8 +315,13 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
     const int hsw = swz<HRC>(l32);   // pt*32 leaves the swizzle unchanged
 
     if (nh > 0) store_vec(vb0);
+    if constexpr (VARLEN) {
+        if ((int)threadIdx.x < Q) sqv[threadIdx.x] = vsq;
+    }
     wait_vmem();
     lds_barrier();
+    int sqj = 0;   // this lane's query token's document (VARLEN)
+    if constexpr (VARLEN) sqj = active ? sqv[rt * 32 + l32] : 0;
 
     // ---- phase B: heads ----
     // One head: start the copies of the next head's tiles into xn / hn (when
@@ -316,6 +339,7 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
     struct Stage {
         V8 m[2];
         float u, d, r;
+        int s;   // key token's document (VARLEN)
         V8 xf[2][PT];
     };
     const int bcl = 8 * ((lane & 15) >> 2) + 4 * (lane >> 5) + (lane & 3);   // key token of this lane's slot
@@ -385,6 +409,7 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
                 st.r = c2v[k * 32 + 31];
                 st.u = (off ? uv : c2v)[k * 32 + bcl];
                 st.d = dtv[k * 32 + bcl];
+                if constexpr (VARLEN) st.s = sqv[k * 32 + bcl];
 #pragma unroll
                 for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
@@ -400,15 +425,19 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
                     const float vj = fast_exp2(c2j - st.r);
                     static_for<16>([&](auto I) {
                         constexpr int idx = decltype(I)::value;
-                        aop[idx >> 3][idx & 7] =
-                            from_f32<T>(row_bcast<idx>(st.u) * (to_f32(st.m[idx >> 3][idx & 7]) * vj));
+                        float val = row_bcast<idx>(st.u) * (to_f32(st.m[idx >> 3][idx & 7]) * vj);
+                        if constexpr (VARLEN)
+                            val = __float_as_int(row_bcast<idx>(__int_as_float(st.s))) == sqj ? val : 0.0f;
+                        aop[idx >> 3][idx & 7] = from_f32<T>(val);
                     });
                 } else {
                     const int dj = jl - (k * 32 + 4 * hf);   // element idx is causal iff 8(idx/4) + idx%4 <= dj
                     static_for<16>([&](auto I) {
                         constexpr int idx = decltype(I)::value;
                         constexpr int off = 8 * (idx >> 2) + (idx & 3);
-                        const float pen = __int_as_float(((dj - off) >> 31) & (int)0xff800000u);
+                        float pen = __int_as_float(((dj - off) >> 31) & (int)0xff800000u);
+                        if constexpr (VARLEN)
+                            pen = __float_as_int(row_bcast<idx>(__int_as_float(st.s))) == sqj ? pen : -INFINITY;
                         aop[idx >> 3][idx & 7] = from_f32<T>(
                             to_f32(cbd[idx >> 3][idx & 7]) * fast_exp2((c2j - row_bcast<idx>(st.u)) + pen) *
                             row_bcast<idx>(st.d));
@@ -576,8 +605,10 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
 
 template <typename T, int PT, int NT, typename ST, int NBX, int NBH, bool CBL>
 static hipError_t launch_sc2(const Params& p, int hpw, int lds, hipStream_t s) {
-    auto kern = p.z ? ssd_chunk_scan_kernel<T, PT, NT, ST, NBX, NBH, CBL, true>
-                    : ssd_chunk_scan_kernel<T, PT, NT, ST, NBX, NBH, CBL, false>;
+    if (p.z && p.seq_idx) return hipErrorInvalidValue;   // no gated instantiation with documents
+    auto kern = p.z         ? ssd_chunk_scan_kernel<T, PT, NT, ST, NBX, NBH, CBL, true, false>
+                : p.seq_idx ? ssd_chunk_scan_kernel<T, PT, NT, ST, NBX, NBH, CBL, false, true>
+                            : ssd_chunk_scan_kernel<T, PT, NT, ST, NBX, NBH, CBL, false, false>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
@@ -617,9 +648,10 @@ static hipError_t launch_sc(const Params& p, hipStream_t s) {
     const int hpw = scan_hpw(p);
     // prefer C B^T in LDS (frees the registers that would hold it), then
     // double-buffered copies
+    const bool vl = p.seq_idx != nullptr;
 #define SSD_SC_TRY(NBX_, NBH_, CBL_)                                                           \
-    if (Cfg::lds(Q, NBX_, NBH_, CBL_) <= kScanMaxLds)                                          \
-        return launch_sc2<T, PT, NT, ST, NBX_, NBH_, CBL_>(p, hpw, Cfg::lds(Q, NBX_, NBH_, CBL_), s);
+    if (Cfg::lds(Q, NBX_, NBH_, CBL_, vl) <= kScanMaxLds)                                      \
+        return launch_sc2<T, PT, NT, ST, NBX_, NBH_, CBL_>(p, hpw, Cfg::lds(Q, NBX_, NBH_, CBL_, vl), s);
     if constexpr (sizeof(T) == 2 && sizeof(ST) == 2) { SSD_SC_TRY(2, 2, true) }
     if constexpr (sizeof(T) == 2) { SSD_SC_TRY(2, 1, true) }
     SSD_SC_TRY(1, 1, true) SSD_SC_TRY(1, 1, false)

@@ -92,8 +92,10 @@ __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t rs, uint32_t voff, u
 constexpr uint32_t kOob = 0x80000000u;   // buffer offset past every range: the copy reads 0
 
 // FUSED: also compute (and write) cs from dt and A, the step of
-// ssd_chunk_cumsum; else read the given cs.
-template <typename T, int PT, int NT, typename ST, bool FUSED>
+// ssd_chunk_cumsum; else read the given cs. VARLEN (with FUSED only): packed
+// documents, w_j = 0 for tokens outside the document of the chunk's last
+// token (the decay is 0 at a document start, "Transformers are SSMs", Knowl 8).
+template <typename T, int PT, int NT, typename ST, bool FUSED, bool VARLEN>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void ssd_chunk_state_kernel(Params p) {
     using Cfg = StateCfg<T, PT, NT>;
     using V8 = typename Vec8<T>::type;
@@ -232,11 +234,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 v[k] = (hq < nh && k < per && lane < nact && j < qc) ? ldg(csr + j) : 0.0f;
             }
         }
+        int slast = 0;
+        const int* sq = VARLEN ? p.seq_idx + b * T_ + t0 : nullptr;
+        if constexpr (VARLEN) slast = sq[qc - 1];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int j = lane * per + k;
-            if (k < per && lane < nact)
-                row[j] = (hq < nh && j < qc) ? exp2f((last - v[k]) * kLog2e) * dtv[k] : 0.0f;
+            if (k < per && lane < nact) {
+                bool keep = hq < nh && j < qc;
+                if constexpr (VARLEN) keep = keep && sq[min(j, qc - 1)] == slast;
+                row[j] = keep ? exp2f((last - v[k]) * kLog2e) * dtv[k] : 0.0f;
+            }
         }
     }
     lds_barrier();
@@ -369,10 +377,14 @@ static hipError_t launch_cs(const Params& p, hipStream_t s) {
     using Cfg = StateCfg<T, PT, NT>;
     const int64_t nhb = (p.heads_per_group + Cfg::HPW - 1) / Cfg::HPW;
     dim3 grid((unsigned)(p.nchunks * p.ngroups * nhb), (unsigned)p.batch);
-    if (p.fuse_cs)
-        hipLaunchKernelGGL((ssd_chunk_state_kernel<T, PT, NT, ST, true>), grid, dim3(256), 0, s, p);
+    if (p.fuse_cs && p.seq_idx)
+        hipLaunchKernelGGL((ssd_chunk_state_kernel<T, PT, NT, ST, true, true>), grid, dim3(256), 0, s, p);
+    else if (p.fuse_cs)
+        hipLaunchKernelGGL((ssd_chunk_state_kernel<T, PT, NT, ST, true, false>), grid, dim3(256), 0, s, p);
+    else if (!p.seq_idx)
+        hipLaunchKernelGGL((ssd_chunk_state_kernel<T, PT, NT, ST, false, false>), grid, dim3(256), 0, s, p);
     else
-        hipLaunchKernelGGL((ssd_chunk_state_kernel<T, PT, NT, ST, false>), grid, dim3(256), 0, s, p);
+        return hipErrorInvalidValue;   // document resets need the fused prefix sums
     return hipGetLastError();
 }
 

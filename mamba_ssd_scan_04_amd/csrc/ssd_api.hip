@@ -178,7 +178,7 @@ ssd_status ssd_chunk_cumsum_state(const ssd_dims* d, const void* x, const float*
 namespace {
 
 ssd_status state_passing_impl(const ssd_dims* d, const float* cs, void* states, const float* init,
-                              float* final_state, hipStream_t stream) {
+                              float* final_state, hipStream_t stream, const int* seq = nullptr) {
     ssd_status st = ssd_check_dims(d);
     if (st != SSD_OK) return st;
     if (!final_state) return SSD_ERR_NULL_POINTER;
@@ -196,12 +196,13 @@ ssd_status state_passing_impl(const ssd_dims* d, const float* cs, void* states, 
     if (!aligned16(cs) || !aligned16(states)) return SSD_ERR_MISALIGNED;
     p.cs = const_cast<float*>(cs);
     p.states = states;
+    p.seq_idx = seq;
     return to_status(ssd::launch_state_passing(p, d->state_dtype, stream));
 }
 
 ssd_status chunk_scan_impl(const ssd_dims* d, const void* x, const float* dt, const void* B, const void* C,
                            const float* D, const float* cs, const void* states, int read_h0, const void* z,
-                           void* y, hipStream_t stream) {
+                           void* y, hipStream_t stream, const int* seq = nullptr) {
     ssd_status st = ssd_check_dims(d);
     if (st != SSD_OK) return st;
     if (empty(d)) return SSD_OK;
@@ -221,12 +222,14 @@ ssd_status chunk_scan_impl(const ssd_dims* d, const void* x, const float* dt, co
     p.read_h0 = read_h0;
     if (z && !aligned16(z)) return SSD_ERR_MISALIGNED;
     p.z = z;
+    p.seq_idx = seq;
     return to_status(ssd::launch_chunk_scan(p, d->dtype, d->state_dtype, stream));
 }
 
 ssd_status forward_impl(const ssd_dims* d, const void* x, const float* dt, const float* A, const void* B,
                         const void* C, const float* D, const float* init, const void* z, void* y,
-                        float* final_state, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                        float* final_state, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                        const int* seq = nullptr) {
     ssd_status st = ssd_check_dims(d);
     if (st != SSD_OK) return st;
     if (d->batch == 0) return SSD_OK;
@@ -240,9 +243,22 @@ ssd_status forward_impl(const ssd_dims* d, const void* x, const float* dt, const
     if (workspace_bytes < ssd_workspace_size(d)) return SSD_ERR_WORKSPACE_TOO_SMALL;
     float* cs = static_cast<float*>(workspace);
     void* states = static_cast<unsigned char*>(workspace) + round_up(cs_bytes_of(d));
-    st = ssd_chunk_cumsum_state(d, x, dt, A, B, cs, states, stream);
-    if (st == SSD_OK) st = state_passing_impl(d, cs, states, init, final_state, stream);
-    if (st == SSD_OK) st = chunk_scan_impl(d, x, dt, B, C, D, cs, states, init ? 1 : 0, z, y, stream);
+    if (seq) {   // the fused chunk-state launch, with the document masks
+        ssd::Params p = make_params(d);
+        p.x = x;
+        p.dt = dt;
+        p.A = A;
+        p.B = B;
+        p.cs = cs;
+        p.states = states;
+        p.fuse_cs = 1;
+        p.seq_idx = seq;
+        st = to_status(ssd::launch_chunk_state(p, d->dtype, d->state_dtype, stream));
+    } else {
+        st = ssd_chunk_cumsum_state(d, x, dt, A, B, cs, states, stream);
+    }
+    if (st == SSD_OK) st = state_passing_impl(d, cs, states, init, final_state, stream, seq);
+    if (st == SSD_OK) st = chunk_scan_impl(d, x, dt, B, C, D, cs, states, init ? 1 : 0, z, y, stream, seq);
     return st;
 }
 
@@ -329,5 +345,22 @@ ssd_status ssd_forward_gated(const ssd_dims* d, const void* x, const float* dt, 
                         stream);
 }
 
-}  // extern "C"
+ssd_status ssd_forward_varlen(const ssd_dims* d, const void* x, const float* dt, const float* A,
+                              const void* B, const void* C, const float* D, const float* initial_state,
+                              const int32_t* seq_idx, void* y, float* final_state, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+    ssd_status st = ssd_check_dims(d);
+    if (st != SSD_OK) return st;
+    if (empty(d)) return forward_impl(d, x, dt, A, B, C, D, initial_state, nullptr, y, final_state, workspace,
+                                      workspace_bytes, stream);
+    if (!seq_idx) return SSD_ERR_NULL_POINTER;
+    if (reinterpret_cast<uintptr_t>(seq_idx) & 3) return SSD_ERR_MISALIGNED;
+    // the chunk scan keeps the chunk's document ids in LDS beside its tiles
+    if (ssd::chunk_scan_lds_bytes(d->dtype, d->state_dtype, d->headdim, d->dstate, d->chunk_size) +
+            4 * d->chunk_size > kMaxLds)
+        return SSD_ERR_UNSUPPORTED;
+    return forward_impl(d, x, dt, A, B, C, D, initial_state, nullptr, y, final_state, workspace, workspace_bytes,
+                        stream, seq_idx);
+}
 
+}  // extern "C"

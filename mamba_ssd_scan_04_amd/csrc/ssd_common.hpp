@@ -45,6 +45,8 @@ struct Params {
     const float* init_state;   // state before the first token [b,H,N,P]; nullptr: zero
     int read_h0;               // chunk_scan applies states[., 0] (h_0) to the first chunk too
     const void* z;             // gate input [b,T,H,P] (x's type): y *= silu(z); nullptr: no gate
+    const int* seq_idx;        // document ids [b,T], non-decreasing along T: the state is reset where
+                               // the id changes; nullptr: one sequence per batch row
 };
 
 // ---- element traits --------------------------------------------------------

@@ -56,7 +56,11 @@ constexpr int kPassElems = 8;        // consecutive state elements per thread
 // The chunk states are read in windows of 8 chunks, the next window's loads
 // issued before the current window is folded (h <- a h + S, storing h before
 // each fold), so up to 16 loads per thread are in flight.
-template <typename ST>
+// VARLEN: packed documents; a chunk in which a document starts (the id of its
+// last token differs from that of the token before the chunk, or from the
+// first token's for chunk 0) passes no state on: its decay is 0 ("Transformers
+// are SSMs", Knowl 8).
+template <typename ST, bool VARLEN>
 __global__ __launch_bounds__(kPassThreads) void ssd_state_passing_kernel(Params p) {
     // the block's rows of the final state, row stride N + 1 (no bank conflicts
     // on the transposed reads); at most 2048 / 16 = 128 rows
@@ -88,12 +92,17 @@ __global__ __launch_bounds__(kPassThreads) void ssd_state_passing_kernel(Params 
     }
     typename O::raw cur[kPassWin], nxt[kPassWin];
     float acur[kPassWin], anxt[kPassWin];
+    const int* sq = VARLEN ? p.seq_idx + b * p.seqlen : nullptr;
     auto load_win = [&](typename O::raw (&w)[kPassWin], float (&a)[kPassWin], int64_t c0) {
 #pragma unroll
         for (int u = 0; u < kPassWin; ++u) {
             const int64_t c = c0 + u < nc ? c0 + u : nc - 1;   // clamped: extra loads repeat the last chunk
             w[u] = O::load(st + c * cstride);
             a[u] = lam[c * Q];
+            if constexpr (VARLEN) {
+                const int64_t tl = min<int64_t>((c + 1) * Q, p.seqlen) - 1, tp = c > 0 ? c * Q - 1 : 0;
+                if (sq[tl] != sq[tp]) a[u] = -INFINITY;   // exp gives exactly 0
+            }
         }
     };
     if (live) load_win(cur, acur, 0);
@@ -143,7 +152,10 @@ static hipError_t launch_sp(const Params& p, hipStream_t s) {
     const int64_t PN = p.headdim * p.dstate;
     const int64_t per_block = (int64_t)kPassThreads * kPassElems;
     dim3 grid((unsigned)((PN + per_block - 1) / per_block), (unsigned)p.nheads, (unsigned)p.batch);
-    hipLaunchKernelGGL((ssd_state_passing_kernel<ST>), grid, dim3(kPassThreads), 0, s, p);
+    if (p.seq_idx)
+        hipLaunchKernelGGL((ssd_state_passing_kernel<ST, true>), grid, dim3(kPassThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL((ssd_state_passing_kernel<ST, false>), grid, dim3(kPassThreads), 0, s, p);
     return hipGetLastError();
 }
 

@@ -140,6 +140,24 @@ def generate_gate(w: Workload, seed: int = 0) -> torch.Tensor:
     return torch.from_numpy(z).to(torch_dtype(w.dtype))
 
 
+def generate_seq_idx(w: Workload, seed: int = 0, docs_per_row: int = 4, cuts=()) -> torch.Tensor:
+    """Document ids [b,T] int32 for rows that pack several documents: per row,
+    docs_per_row - 1 document starts drawn uniformly from 1 .. T-1 without
+    repetition, plus the starts listed in `cuts` (those inside the row); ids
+    count the starts so far plus 1000 * row (they never decrease along T)."""
+    rng = np.random.default_rng(seed + 15485863)
+    b, T = w.batch, w.seqlen
+    ids = np.zeros((b, T), dtype=np.int32)
+    for r in range(b):
+        k = min(max(docs_per_row - 1, 0), max(T - 1, 0))
+        starts = set(rng.choice(np.arange(1, T), size=k, replace=False).tolist()) if k > 0 else set()
+        starts |= {int(c) for c in cuts if 0 < c < T}
+        flags = np.zeros(T, dtype=np.int32)
+        flags[sorted(starts)] = 1
+        ids[r] = np.cumsum(flags) + 1000 * r
+    return torch.from_numpy(ids)
+
+
 def to_float64(inp: dict) -> dict:
     """Exact upcast of the stored bits to float64 numpy arrays."""
     return {k: v.float().numpy().astype(np.float64) for k, v in inp.items()}

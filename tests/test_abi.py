@@ -224,3 +224,21 @@ def test_peak_probe_library_exports():
     assert peak.ssd_peak_mfma_bf16(4, 10, None, None) != 0
     assert peak.ssd_peak_stream(_fake(0x1000), _fake(0x2000), 0, 4, None) != 0
     assert peak.ssd_peak_stream(_fake(0x1008), _fake(0x2000), 16, 4, None) != 0
+
+
+def test_varlen_forward_argument_errors(lib):
+    d = dims()
+    ws = ssd.ssd_workspace_size(d)
+    good = [_fake(0x500000 * (i + 1)) for i in range(11)]
+    x, dt, A, B, C, D, seq, y, fin, work = good[:10]
+    f = lib.ssd_forward_varlen
+    P = ctypes.byref
+    assert f(P(d), x, dt, A, B, C, D, None, None, y, fin, work, ws, None) == NULLP    # seq_idx required
+    assert f(P(d), x, dt, A, B, C, D, None, _fake(0x500002), y, fin, work, ws, None) == MISAL
+    assert f(P(d), x, dt, A, B, C, D, None, seq, y, fin, work, ws - 1, None) == WS
+    assert f(P(d), None, dt, A, B, C, D, None, seq, y, fin, work, ws, None) == NULLP
+    assert f(P(dims(ngroups=3)), x, dt, A, B, C, D, None, seq, y, fin, work, ws, None) == SHAPE
+    # every shape the plain forward accepts leaves room for the chunk's ids in LDS
+    big = dims(headdim=128, dstate=256, chunk_size=64)
+    assert f(P(big), x, dt, A, B, C, D, None, seq, y, fin, work, ssd.ssd_workspace_size(big) - 1, None) == WS
+    assert f(P(dims(batch=0)), None, None, None, None, None, None, None, None, None, None, None, 0, None) == OK

@@ -60,3 +60,16 @@ def test_float64_upcast_is_exact():
     assert f["x"].dtype == np.float64
     back = torch.from_numpy(f["x"]).to(torch.bfloat16)
     assert torch.equal(back, d["x"])
+
+
+def test_seq_idx_generator():
+    w = inputs.WORKLOADS["m125"].replace(batch=3, seqlen=300)
+    s1 = inputs.generate_seq_idx(w, 5, 6, cuts=(256, 299, 400))
+    assert s1.dtype == torch.int32 and tuple(s1.shape) == (3, 300)
+    d = s1[:, 1:] - s1[:, :-1]
+    assert bool(((d == 0) | (d == 1)).all())            # ids never decrease, one start at a time
+    assert bool((s1[:, 256] != s1[:, 255]).all()) and bool((s1[:, 299] != s1[:, 298]).all())
+    assert int((d == 1).sum(dim=1).min()) >= 6          # 5 drawn starts plus the cuts inside the row
+    assert torch.equal(s1, inputs.generate_seq_idx(w, 5, 6, cuts=(256, 299, 400)))
+    assert bool((s1[1] >= 1000).all()) and bool((s1[0] < 1000).all())
+
