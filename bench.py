@@ -15,7 +15,8 @@ forward with warm caches and with a 512 MB scrub written between calls (cold
 last-level cache); the path's bytes against the HBM peak, both the method's
 compulsory bytes and the four-kernel design's; the attainable peaks of a bare
 MFMA loop and a bare streaming copy on this chip; the other storage type of
-the inter-chunk states; the gated forward; and the decoding step.
+the inter-chunk states; the gated forward; the forward over rows packing
+several documents; and the decoding step.
 """
 from __future__ import annotations
 
@@ -207,15 +208,18 @@ def cpu_baseline(inp, w, budget_s: float = 10.0) -> dict:
 
 
 def _counter_means(path: str, counter: str) -> dict:
-    """Mean counter value per kernel name from a rocprofv3 counter_collection.csv."""
+    """Per kernel name in a rocprofv3 counter_collection.csv: (mean counter
+    value, first dispatch id)."""
     import csv
-    acc = {}
+    acc, first = {}, {}
     with open(path) as f:
         for r in csv.DictReader(f):
             if r["Counter_Name"] != counter:
                 continue
-            acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
-    return {k: sum(v) / len(v) for k, v in acc.items()}
+            name = r["Kernel_Name"]
+            acc.setdefault(name, []).append(float(r["Counter_Value"]))
+            first[name] = min(first.get(name, 1 << 62), int(r["Dispatch_Id"]))
+    return {k: (sum(v) / len(v), first[k]) for k, v in acc.items()}
 
 
 def record_traffic(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, workload, state_dtype) -> int:
@@ -223,7 +227,13 @@ def record_traffic(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, workload,
     WRITE_SIZE, KiB per dispatch) into HBM bytes per launch of each kernel,
     scaling each counter by what it reads for the 1 GiB copy of
     --calibrate-copy, and write profiles/pmc_<kernel>_<workload>_<state>.json
-    tagged with the hash of the kernel source it was taken on."""
+    tagged with the hash of the kernel source it was taken on.
+
+    The instantiations are told apart by the order in which this script first
+    launches them (the profiler prints some template names garbled): for each
+    kernel, the first name is ssd_forward with the default state storage
+    (bf16 for bf16 inputs), the second ssd_forward with the other storage;
+    the gated and packed-document instantiations come after both."""
     from mamba_ssd_scan_04_amd import inputs
     nbytes = 1 << 30
     cf = _counter_means(cal_fetch_csv, "FETCH_SIZE")
@@ -232,47 +242,23 @@ def record_traffic(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, workload,
     if not copy:
         print("no copy kernel in the calibration runs", file=sys.stderr)
         return 1
-    f_scale = nbytes / (cf[copy[0]] * 1024.0)
-    w_scale = nbytes / (cw[copy[0]] * 1024.0)
+    f_scale = nbytes / (cf[copy[0]][0] * 1024.0)
+    w_scale = nbytes / (cw[copy[0]][0] * 1024.0)
     fe, wr = _counter_means(fetch_csv, "FETCH_SIZE"), _counter_means(write_csv, "WRITE_SIZE")
     w = inputs.WORKLOADS[workload]
     work = kernel_work(w, 2 if state_dtype == "bf16" else 4)
-    import re
-
-    def state_of(name):
-        """Storage type of the inter-chunk states a dispatch was instantiated
-        for, read from its (mangled or demangled) template arguments."""
-        if "state_passing" in name:
-            return "bf16" if ("IDF16bEE" in name or "<__bf16>" in name) else "fp32"
-        m = re.search(r"Li\d+ELi\d+E(DF16b|f)", name)
-        if m is not None:
-            return {"DF16b": "bf16", "f": "fp32"}[m.group(1)]
-        # the profiler's demangler garbles some of these names; the state
-        # type argument survives as "EDF1..." (bf16) or "EfL..." (fp32)
-        if "EDF1" in name:
-            return "bf16"
-        if "EfL" in name:
-            return "fp32"
-        return None
-
-    def gated(name):
-        """The chunk scan's instantiation with the fused output gate (its last
-        template argument): not what ssd_forward runs."""
-        m = re.search(r"Lb[01]ELb([01])EEEv", name)
-        if m is not None:
-            return m.group(1) == "1"
-        return bool(re.search(r"\btrue>\(ssd::Params", name))
+    default = "bf16" if w.dtype == "bf16" else "fp32"
+    rank = 0 if state_dtype == default else 1
 
     for kern in KERNELS:
-        names = [k for k in fe if kern + "_kernel" in k and not (kern == "ssd_chunk_scan" and gated(k))]
-        if kern != "ssd_chunk_cumsum":
-            names = [k for k in names if state_of(k) == state_dtype]
-        if len(names) != 1 or names[0] not in wr:
-            print(f"{kern}: expected one matching dispatch name, got {names}", file=sys.stderr)
+        names = sorted((k for k in fe if kern + "_kernel" in k), key=lambda k: fe[k][1])
+        if len(names) <= rank or names[rank] not in wr:
+            print(f"{kern}: no dispatch name for {state_dtype} states among {names}", file=sys.stderr)
             continue
-        rd = fe[names[0]] * 1024.0 * f_scale
-        wb = wr[names[0]] * 1024.0 * w_scale
-        rec = {"kernel": kern, "dispatch_name": names[0], "workload": workload, "state_dtype": state_dtype,
+        name = names[rank]
+        rd = fe[name][0] * 1024.0 * f_scale
+        wb = wr[name][0] * 1024.0 * w_scale
+        rec = {"kernel": kern, "dispatch_name": name, "workload": workload, "state_dtype": state_dtype,
                "source_sha": source_sha(kern), "fetch_scale": round(f_scale, 4),
                "write_scale": round(w_scale, 4), "hbm_read_bytes_per_launch": int(rd),
                "hbm_write_bytes_per_launch": int(wb), "hbm_bytes_per_launch": int(rd + wb),
@@ -451,6 +437,25 @@ def main() -> int:
     gated_ms = (time.perf_counter() - tg) * 1e3 / args.steps
     del zg, yg
 
+    # packed documents (ssd_forward_varlen): the same rows holding 8 documents
+    # each, the state reset at every document start
+    seq = inputs.generate_seq_idx(w, 45, 8).to(dev)
+    yv = torch.empty_like(g["x"])
+
+    def varlen():
+        ssd.ssd_forward_varlen(d, g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], None, seq, yv, final, ws,
+                               ws.numel(), sh)
+
+    for _ in range(args.warmup):
+        varlen()
+    torch.cuda.synchronize()
+    tv = time.perf_counter()
+    for _ in range(args.steps):
+        varlen()
+    torch.cuda.synchronize()
+    varlen_ms = (time.perf_counter() - tv) * 1e3 / args.steps
+    del yv, seq
+
     # the decoding step (ssd_step) at the same layer shape: one token per
     # sequence, the fp32 state read and written in place
     dstep = ssd.make_dims(w.batch, 1, w.nheads, w.headdim, w.dstate, w.ngroups, 32, w.dtype, "fp32")
@@ -523,6 +528,8 @@ def main() -> int:
         "other_state_storage": alt,
         "gated": {"entry": "ssd_forward_gated", "ms_per_step": round(gated_ms, 5),
                   "tokens_per_s": round(w.batch * w.seqlen / (gated_ms * 1e-3), 1)},
+        "varlen": {"entry": "ssd_forward_varlen", "documents_per_row": 8, "ms_per_step": round(varlen_ms, 5),
+                   "tokens_per_s": round(w.batch * w.seqlen / (varlen_ms * 1e-3), 1)},
         "decode": decode,
         "cpu_baseline": None,
     }
