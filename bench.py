@@ -16,7 +16,8 @@ last-level cache); the path's bytes against the HBM peak, both the method's
 compulsory bytes and the four-kernel design's; the attainable peaks of a bare
 MFMA loop and a bare streaming copy on this chip; the other storage type of
 the inter-chunk states; the gated forward; the forward over rows packing
-several documents; and the decoding step.
+several documents; one GPU's share of an 8-way context-parallel forward; and
+the decoding step.
 """
 from __future__ import annotations
 
@@ -456,6 +457,42 @@ def main() -> int:
     varlen_ms = (time.perf_counter() - tv) * 1e3 / args.steps
     del yv, seq
 
+    # context parallelism as one of 8 GPUs would run it (Knowl 8): its share
+    # is T/8 tokens of every row; it runs them from a zero state, forms its
+    # total log-decay, folds the 8 shards' boundary states (which the GPUs
+    # would all-gather first) and runs its tokens again from its entering state
+    K = 8
+    Ts = w.seqlen // K
+    shard = {k: g[k][:, :Ts].contiguous() for k in ("x", "dt", "B", "C")}
+    ds = ssd.dims_of(shard["x"], shard["B"], w.chunk_size, args.state_dtype)
+    wss = ssd.alloc_workspace(ds, dev)
+    ys = torch.empty_like(shard["x"])
+    fins = torch.zeros((K, w.batch, w.nheads, w.dstate, w.headdim), dtype=torch.float32, device=dev)
+    tots = torch.zeros((K, w.batch, w.nheads), dtype=torch.float32, device=dev)
+    ent = torch.empty((K + 1, w.batch, w.nheads, w.dstate, w.headdim), dtype=torch.float32, device=dev)
+
+    def share():
+        ssd.ssd_forward(ds, shard["x"], shard["dt"], g["A"], shard["B"], shard["C"], g["D"], ys, fins[0], wss,
+                        wss.numel(), sh)
+        ssd.ssd_total_decay(ds, shard["dt"], g["A"], tots[0], sh)
+        ssd.ssd_fold_states(ds, K, tots, fins, None, ent, sh)
+        ssd.ssd_forward_init(ds, shard["x"], shard["dt"], g["A"], shard["B"], shard["C"], g["D"], ent[K - 1], ys,
+                             fins[0], wss, wss.numel(), sh)
+
+    for _ in range(args.warmup):
+        share()
+    torch.cuda.synchronize()
+    tc = time.perf_counter()
+    for _ in range(args.steps):
+        share()
+    torch.cuda.synchronize()
+    share_ms = (time.perf_counter() - tc) * 1e3 / args.steps
+    cp = {"shards": K, "tokens_per_shard_row": Ts, "share_ms": round(share_ms, 5),
+          "what": "one GPU's share of an 8-way context-parallel forward without the all-gather: its T/8 tokens "
+                  "from a zero state, its total log-decay, the 8-shard state fold, its tokens again from the "
+                  "entering state"}
+    del shard, wss, ys, fins, tots, ent
+
     # the decoding step (ssd_step) at the same layer shape: one token per
     # sequence, the fp32 state read and written in place
     dstep = ssd.make_dims(w.batch, 1, w.nheads, w.headdim, w.dstate, w.ngroups, 32, w.dtype, "fp32")
@@ -530,6 +567,7 @@ def main() -> int:
                   "tokens_per_s": round(w.batch * w.seqlen / (gated_ms * 1e-3), 1)},
         "varlen": {"entry": "ssd_forward_varlen", "documents_per_row": 8, "ms_per_step": round(varlen_ms, 5),
                    "tokens_per_s": round(w.batch * w.seqlen / (varlen_ms * 1e-3), 1)},
+        "context_parallel": cp,
         "decode": decode,
         "cpu_baseline": None,
     }

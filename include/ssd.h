@@ -165,6 +165,42 @@ ssd_status ssd_forward_varlen(const ssd_dims* d, const void* x, const float* dt,
                               size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Sequence (context) parallelism ("Transformers are SSMs", Knowl 8): a long
+ * sequence cut along T into K shards, each run on its own tokens, with only
+ * the boundary state passed from one shard to the next. The shard-level chain
+ * is the state passing of Knowl 2 one level up:
+ *   H_0 = initial state (or 0),  H_{k+1} = exp(Lambda_k) H_k + F_k,
+ * where F_k is shard k's final state when run from a zero state
+ * (ssd_forward) and Lambda_k = sum over its tokens of dt_t A_h, the log of
+ * the product of its decays. Running shard k from H_k (ssd_forward_init)
+ * then gives its exact output; H_K is the final state of the whole sequence.
+ */
+
+/*
+ * Lambda for one shard: total[b,h] = A[h] * sum_t dt[b,t,h] (fp32, the sum
+ * in a fixed order). d gives batch, seqlen (the shard's T), nheads, headdim
+ * and dstate (the last two only checked); dt [b,T,H] fp32, A [H] fp32,
+ * total [b,H] fp32 (device, 16-byte aligned). T = 0 writes zeros. Errors:
+ * SSD_ERR_NULL_POINTER, SSD_ERR_BAD_SHAPE (negative sizes, H, N or P < 1),
+ * SSD_ERR_UNSUPPORTED (P or N outside the supported lists),
+ * SSD_ERR_MISALIGNED.
+ */
+ssd_status ssd_total_decay(const ssd_dims* d, const float* dt, const float* A, float* total,
+                           hipStream_t stream);
+
+/*
+ * The shard chain for nshards = K >= 0 shards: totals [K,b,H] (Lambda_k, as
+ * from ssd_total_decay), shard_finals [K,b,H,N,P] (F_k), initial_state
+ * [b,H,N,P] or NULL for zero; entering [K+1,b,H,N,P] receives H_0 .. H_K
+ * (H_k enters shard k; H_K is the final state). All fp32 device buffers,
+ * 16-byte aligned, caller-owned; entering must not overlap the inputs. d gives
+ * batch, nheads, headdim and dstate (seqlen, chunk_size and the dtypes are
+ * ignored). Errors as ssd_total_decay, plus SSD_ERR_BAD_SHAPE for K < 0.
+ */
+ssd_status ssd_fold_states(const ssd_dims* d, int64_t nshards, const float* totals, const float* shard_finals,
+                           const float* initial_state, float* entering, hipStream_t stream);
+
+/*
  * One token of the recurrence, for decoding ("Transformers are SSMs", Knowl 1,
  * the recurrent form one step at a time: the inference mode with O(N P) state
  * per head):

@@ -70,6 +70,9 @@ def load_library() -> ctypes.CDLL:
     lib.ssd_forward_gated.restype = st
     lib.ssd_forward_varlen.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.ssd_forward_varlen.restype = st
+    lib.ssd_total_decay.argtypes, lib.ssd_total_decay.restype = [P, vp, vp, vp, vp], st
+    lib.ssd_fold_states.argtypes = [P, ctypes.c_int64, vp, vp, vp, vp, vp]
+    lib.ssd_fold_states.restype = st
     lib.ssd_chunk_cumsum.argtypes, lib.ssd_chunk_cumsum.restype = [P, vp, vp, vp, vp], st
     lib.ssd_chunk_state.argtypes, lib.ssd_chunk_state.restype = [P, vp, vp, vp, vp, vp, vp], st
     lib.ssd_chunk_cumsum_state.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
@@ -182,6 +185,17 @@ def ssd_forward_varlen(d, x, dt, A, B, C, D, initial_state, seq_idx, y, final_st
                                              _ptr(final_state), _ptr(workspace), workspace_bytes, s))
 
 
+def ssd_total_decay(d, dt, A, total, stream=None):
+    s = _stream(total.device) if stream is None else stream
+    _check(load_library().ssd_total_decay(ctypes.byref(d), _ptr(dt), _ptr(A), _ptr(total), s))
+
+
+def ssd_fold_states(d, nshards, totals, shard_finals, initial_state, entering, stream=None):
+    s = _stream(entering.device) if stream is None else stream
+    _check(load_library().ssd_fold_states(ctypes.byref(d), nshards, _ptr(totals), _ptr(shard_finals),
+                                          _ptr(initial_state), _ptr(entering), s))
+
+
 def ssd_chunk_cumsum(d, dt, A, cs, stream=None):
     s = _stream(dt.device) if stream is None else stream
     _check(load_library().ssd_chunk_cumsum(ctypes.byref(d), _ptr(dt), _ptr(A), _ptr(cs), s))
@@ -280,6 +294,37 @@ def forward(x, dt, A, B, C, D, chunk_size: int, state_dtype: str | None = None, 
             raise ValueError(f"initial_state must be float32 {tuple(final.shape)}")
         ssd_forward_init(d, x, dt, A, B, C, D, initial_state, y, final, workspace, workspace.numel())
     return y, final
+
+
+def forward_sharded(x, dt, A, B, C, D, chunk_size: int, bounds, state_dtype: str | None = None,
+                    initial_state=None):
+    """The forward of one long sequence cut along T at `bounds` (shard k is
+    tokens bounds[k] .. bounds[k+1]-1; bounds[0] = 0, bounds[-1] = T), run
+    the way context parallelism runs it (Knowl 8), here with every shard on
+    this device: each shard from a zero state (ssd_forward) for its final
+    state, its total log-decay (ssd_total_decay), the shard chain
+    (ssd_fold_states), then each shard again from its entering state
+    (ssd_forward_init). Returns y, final_state (as forward())."""
+    K = len(bounds) - 1
+    if K < 1 or bounds[0] != 0 or bounds[-1] != x.shape[1] or any(bounds[k] >= bounds[k + 1] for k in range(K)):
+        raise ValueError("bounds must rise strictly from 0 to T")
+    b, H, P, N = x.shape[0], x.shape[2], x.shape[3], B.shape[3]
+    dev = x.device
+    sl = lambda v, k: v[:, bounds[k]:bounds[k + 1]].contiguous()
+    finals = torch.empty((K, b, H, N, P), dtype=torch.float32, device=dev)
+    totals = torch.empty((K, b, H), dtype=torch.float32, device=dev)
+    for k in range(K):
+        _, finals[k] = forward(sl(x, k), sl(dt, k), A, sl(B, k), sl(C, k), D, chunk_size, state_dtype)
+        d = dims_of(sl(x, k), B, chunk_size, state_dtype or ("bf16" if x.dtype == torch.bfloat16 else "fp32"))
+        tk = torch.empty((b, H), dtype=torch.float32, device=dev)   # its own 16-byte aligned buffer
+        ssd_total_decay(d, sl(dt, k), A, tk)
+        totals[k] = tk
+    entering = torch.empty((K + 1, b, H, N, P), dtype=torch.float32, device=dev)
+    d = dims_of(x, B, chunk_size, state_dtype or ("bf16" if x.dtype == torch.bfloat16 else "fp32"))
+    ssd_fold_states(d, K, totals, finals, initial_state, entering)
+    ys = [forward(sl(x, k), sl(dt, k), A, sl(B, k), sl(C, k), D, chunk_size, state_dtype,
+                  initial_state=entering[k])[0] for k in range(K)]
+    return torch.cat(ys, dim=1), entering[K].clone()
 
 
 def step(x, dt, A, B, C, D, state):

@@ -363,4 +363,41 @@ ssd_status ssd_forward_varlen(const ssd_dims* d, const void* x, const float* dt,
                         stream, seq_idx);
 }
 
+// shapes of a per-head state: b >= 0, H, N, P in the supported lists
+static ssd_status check_state_dims(const ssd_dims* d) {
+    static const int64_t kP[] = {16, 32, 64, 128};
+    static const int64_t kN[] = {16, 32, 64, 128, 256};
+    if (!d) return SSD_ERR_NULL_POINTER;
+    if (d->batch < 0 || d->nheads <= 0 || d->headdim <= 0 || d->dstate <= 0) return SSD_ERR_BAD_SHAPE;
+    if (!in_list(d->headdim, kP, 4) || !in_list(d->dstate, kN, 5)) return SSD_ERR_UNSUPPORTED;
+    if (d->nheads > 65535 * 64 || d->batch > 65535) return SSD_ERR_UNSUPPORTED;
+    return SSD_OK;
+}
+
+ssd_status ssd_total_decay(const ssd_dims* d, const float* dt, const float* A, float* total, hipStream_t stream) {
+    ssd_status st = check_state_dims(d);
+    if (st != SSD_OK) return st;
+    if (d->seqlen < 0) return SSD_ERR_BAD_SHAPE;
+    if (d->batch == 0) return SSD_OK;
+    if (!A || !total || (d->seqlen > 0 && !dt)) return SSD_ERR_NULL_POINTER;
+    if (!aligned16(A) || !aligned16(total) || (dt && !aligned16(dt))) return SSD_ERR_MISALIGNED;
+    if (d->seqlen == 0) return to_status(ssd::launch_zero_fill(total, d->batch * d->nheads, stream));
+    return to_status(ssd::launch_total_decay(dt, A, total, d->batch, d->seqlen, d->nheads, stream));
+}
+
+ssd_status ssd_fold_states(const ssd_dims* d, int64_t nshards, const float* totals, const float* shard_finals,
+                           const float* initial_state, float* entering, hipStream_t stream) {
+    ssd_status st = check_state_dims(d);
+    if (st != SSD_OK) return st;
+    if (nshards < 0) return SSD_ERR_BAD_SHAPE;
+    if (d->batch == 0) return SSD_OK;
+    if (!entering || (nshards > 0 && (!totals || !shard_finals))) return SSD_ERR_NULL_POINTER;
+    if (!aligned16(entering) || (totals && !aligned16(totals)) || (shard_finals && !aligned16(shard_finals)) ||
+        (initial_state && !aligned16(initial_state)))
+        return SSD_ERR_MISALIGNED;
+    const int64_t bh = d->batch * d->nheads, np = d->dstate * d->headdim;
+    if (bh * np / 4 / 256 >= (int64_t)INT32_MAX) return SSD_ERR_UNSUPPORTED;
+    return to_status(ssd::launch_fold(nshards, bh, np, totals, shard_finals, initial_state, entering, stream));
+}
+
 }  // extern "C"

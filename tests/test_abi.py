@@ -242,3 +242,20 @@ def test_varlen_forward_argument_errors(lib):
     big = dims(headdim=128, dstate=256, chunk_size=64)
     assert f(P(big), x, dt, A, B, C, D, None, seq, y, fin, work, ssd.ssd_workspace_size(big) - 1, None) == WS
     assert f(P(dims(batch=0)), None, None, None, None, None, None, None, None, None, None, None, 0, None) == OK
+
+
+def test_shard_entry_points_argument_errors(lib):
+    P = ctypes.byref
+    a = _fake(0x600000)
+    d = dims()
+    assert lib.ssd_total_decay(None, a, a, a, None) == NULLP
+    assert lib.ssd_total_decay(P(d), None, a, a, None) == NULLP
+    assert lib.ssd_total_decay(P(d), a, a, _fake(0x600004), None) == MISAL
+    assert lib.ssd_total_decay(P(dims(headdim=40)), a, a, a, None) == UNSUP
+    assert lib.ssd_total_decay(P(dims(batch=0)), None, None, None, None) == OK
+    assert lib.ssd_fold_states(P(d), -1, a, a, None, a, None) == SHAPE
+    assert lib.ssd_fold_states(P(d), 4, None, a, None, a, None) == NULLP
+    assert lib.ssd_fold_states(P(d), 4, a, a, None, None, None) == NULLP
+    assert lib.ssd_fold_states(P(d), 4, a, a, _fake(0x600008), a, None) == MISAL
+    assert lib.ssd_fold_states(P(dims(nheads=0)), 4, a, a, None, a, None) == SHAPE
+    assert lib.ssd_fold_states(P(dims(batch=0)), 4, None, None, None, None, None) == OK
