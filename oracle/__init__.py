@@ -223,6 +223,28 @@ def silu_gate(y, z):
         return y * (z / (1.0 + np.exp(-z)))
 
 
+def gated_rmsnorm(y, z, weight, eps: float, groups: int = 1):
+    """The normalisation after the gate in the Mamba-2 block ("Transformers are
+    SSMs", Knowl 6: Y_g = Y * SiLU(z), then GroupNorm or RMSNorm before the
+    output projection), fp64. Per token, the e*d = H*P channels of y [b,T,H,P]
+    are cut into `groups` equal contiguous groups (1: plain RMSNorm over all
+    channels; Knowl 8's GroupNorm with groups divisible by the TP degree), and
+    each group is divided by its root mean square:
+        g   = y * silu(z)   (y itself when z is None)
+        out = g / sqrt(mean over the group of g^2 + eps) * weight[channel]
+    weight is [H*P]."""
+    y = np.asarray(y, dtype=np.float64)
+    g = y if z is None else silu_gate(y, z)
+    b, T, H, P = g.shape
+    C = H * P
+    if C % groups != 0:
+        raise ValueError("groups must divide H*P")
+    v = g.reshape(b, T, groups, C // groups)
+    ms = np.mean(v * v, axis=-1, keepdims=True)
+    out = (v / np.sqrt(ms + eps)).reshape(b, T, C) * np.asarray(weight, dtype=np.float64)[None, None, :]
+    return out.reshape(b, T, H, P)
+
+
 def rel_err(got, ref) -> float:
     """max |got - ref| / max |ref| (0 when both are all zero)."""
     got = np.asarray(got, dtype=np.float64)

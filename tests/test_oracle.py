@@ -396,6 +396,37 @@ def test_varlen_one_document_is_the_plain_recurrence(oracle_mod):
     np.testing.assert_array_equal(fin, fin0)
 
 
+def test_gated_rmsnorm_pins(oracle_mod):
+    """The normalisation after the gate (Knowl 6): a constant group maps to the
+    weights; with eps = 0 a positive rescaling of y leaves the output unchanged
+    and every group of the unweighted output has mean square 1; with one group
+    and no gate it is torch's own RMSNorm (a library routine); the gate enters
+    as y * silu(z)."""
+    import torch
+
+    rng = np.random.default_rng(60)
+    b, T, H, P = 2, 5, 3, 4
+    y = rng.standard_normal((b, T, H, P))
+    z = rng.standard_normal((b, T, H, P))
+    w = rng.standard_normal(H * P)
+    ones = np.ones(H * P)
+    const = np.full((b, T, H, P), 2.5)
+    np.testing.assert_allclose(oracle_mod.gated_rmsnorm(const, None, w, 0.0, 3),
+                               np.broadcast_to(w.reshape(H, P), (b, T, H, P)), rtol=0, atol=1e-14)
+    for groups in (1, 2, 3, 6):
+        a = oracle_mod.gated_rmsnorm(y, z, w, 0.0, groups)
+        np.testing.assert_allclose(oracle_mod.gated_rmsnorm(7.0 * y, z, w, 0.0, groups), a, rtol=1e-13, atol=1e-13)
+        u = oracle_mod.gated_rmsnorm(y, z, ones, 0.0, groups).reshape(b, T, groups, -1)
+        np.testing.assert_allclose(np.mean(u * u, axis=-1), 1.0, rtol=1e-13)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(y.reshape(b, T, H * P)), (H * P,),
+                                       torch.from_numpy(w), eps=1e-5).numpy()
+    np.testing.assert_allclose(oracle_mod.gated_rmsnorm(y, None, w, 1e-5, 1).reshape(b, T, H * P), ref,
+                               rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(oracle_mod.gated_rmsnorm(y, z, w, 1e-5, 2),
+                               oracle_mod.gated_rmsnorm(oracle_mod.silu_gate(y, z), None, w, 1e-5, 2),
+                               rtol=1e-13, atol=1e-13)
+
+
 def test_silu_gate_identities(oracle_mod):
     """silu(z) = z sigma(z): pinned by sigma(z) + sigma(-z) = 1, i.e.
     silu(z) - silu(-z) = z, by the tanh form z (1 + tanh(z/2)) / 2 (a library
