@@ -15,7 +15,8 @@ forward with warm caches and with a 512 MB scrub written between calls (cold
 last-level cache); the path's bytes against the HBM peak, both the method's
 compulsory bytes and the four-kernel design's; the attainable peaks of a bare
 MFMA loop and a bare streaming copy on this chip; the other storage type of
-the inter-chunk states; the gated forward; the forward over rows packing
+the inter-chunk states; the gated forward, alone and followed by the
+RMSNorm in place; the forward over rows packing
 several documents; one GPU's share of an 8-way context-parallel forward; and
 the decoding step.
 """
@@ -436,7 +437,24 @@ def main() -> int:
         gated()
     torch.cuda.synchronize()
     gated_ms = (time.perf_counter() - tg) * 1e3 / args.steps
-    del zg, yg
+    # and the normalisation after the gate (RMSNorm over each token's H*P
+    # channels, synthetic weights) in place on the gated output
+    wn = torch.randn(w.nheads * w.headdim, generator=torch.Generator().manual_seed(2)).to(dev)
+    dn = ssd.make_dims(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk_size, w.dtype, "fp32")
+
+    def gated_norm():
+        gated()
+        ssd.ssd_gated_rmsnorm(dn, yg, None, wn, 1e-5, 1, yg, sh)
+
+    for _ in range(args.warmup):
+        gated_norm()
+    torch.cuda.synchronize()
+    tn = time.perf_counter()
+    for _ in range(args.steps):
+        gated_norm()
+    torch.cuda.synchronize()
+    gated_norm_ms = (time.perf_counter() - tn) * 1e3 / args.steps
+    del zg, yg, wn
 
     # packed documents (ssd_forward_varlen): the same rows holding 8 documents
     # each, the state reset at every document start
@@ -564,7 +582,8 @@ def main() -> int:
         "evented_ms_per_step": round(staged_ms, 5),
         "other_state_storage": alt,
         "gated": {"entry": "ssd_forward_gated", "ms_per_step": round(gated_ms, 5),
-                  "tokens_per_s": round(w.batch * w.seqlen / (gated_ms * 1e-3), 1)},
+                  "tokens_per_s": round(w.batch * w.seqlen / (gated_ms * 1e-3), 1),
+                  "with_rmsnorm_ms_per_step": round(gated_norm_ms, 5)},
         "varlen": {"entry": "ssd_forward_varlen", "documents_per_row": 8, "ms_per_step": round(varlen_ms, 5),
                    "tokens_per_s": round(w.batch * w.seqlen / (varlen_ms * 1e-3), 1)},
         "context_parallel": cp,

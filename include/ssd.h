@@ -143,6 +143,27 @@ ssd_status ssd_forward_gated(const ssd_dims* d, const void* x, const float* dt, 
                              size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * The normalisation after the gate in the Mamba-2 block ("Transformers are
+ * SSMs", Knowl 6: Y * SiLU(z), then a group or RMS norm before the output
+ * projection; Knowl 8: the norm in groups whose count divides the
+ * tensor-parallel degree). Per token, the H*P channels of y [b,T,H,P] are cut
+ * into `groups` equal contiguous groups (1: RMSNorm over all channels):
+ *   g = y * silu(z)  (y itself when z is NULL),
+ *   out = g / sqrt(mean over the group of g^2 + eps) * weight[channel].
+ * y, z and out are in d->dtype, [b,T,H,P]; weight [H*P] fp32; all device,
+ * caller-owned, 16-byte aligned. out may be y (in place) but must not
+ * otherwise overlap the inputs. eps is used as given. d gives batch, seqlen,
+ * nheads, headdim and dtype (dstate, ngroups, chunk_size and state_dtype are
+ * ignored). After ssd_forward_gated, a call with z = NULL and out = y
+ * normalises the gated output in place. Errors: SSD_ERR_NULL_POINTER,
+ * SSD_ERR_BAD_SHAPE (negative sizes, H or P < 1, groups < 1 or not dividing
+ * H*P), SSD_ERR_UNSUPPORTED (unknown dtype, or a group size not a multiple
+ * of 8 channels), SSD_ERR_MISALIGNED.
+ */
+ssd_status ssd_gated_rmsnorm(const ssd_dims* d, const void* y, const void* z, const float* weight, float eps,
+                             int64_t groups, void* out, hipStream_t stream);
+
+/*
  * Full forward over rows that pack several documents ("Transformers are SSMs",
  * Knowl 8: variable-length sequences concatenated, the state reset between
  * them by a zero decay at each document start). seq_idx [b,T] int32 (device,

@@ -71,6 +71,8 @@ def load_library() -> ctypes.CDLL:
     lib.ssd_forward_varlen.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.ssd_forward_varlen.restype = st
     lib.ssd_total_decay.argtypes, lib.ssd_total_decay.restype = [P, vp, vp, vp, vp], st
+    lib.ssd_gated_rmsnorm.argtypes = [P, vp, vp, vp, ctypes.c_float, ctypes.c_int64, vp, vp]
+    lib.ssd_gated_rmsnorm.restype = st
     lib.ssd_fold_states.argtypes = [P, ctypes.c_int64, vp, vp, vp, vp, vp]
     lib.ssd_fold_states.restype = st
     lib.ssd_chunk_cumsum.argtypes, lib.ssd_chunk_cumsum.restype = [P, vp, vp, vp, vp], st
@@ -183,6 +185,27 @@ def ssd_forward_varlen(d, x, dt, A, B, C, D, initial_state, seq_idx, y, final_st
     _check(load_library().ssd_forward_varlen(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
                                              _ptr(C), _ptr(D), _ptr(initial_state), _ptr(seq_idx), _ptr(y),
                                              _ptr(final_state), _ptr(workspace), workspace_bytes, s))
+
+
+def ssd_gated_rmsnorm(d, y, z, weight, eps, groups, out, stream=None):
+    s = _stream(out.device) if stream is None else stream
+    _check(load_library().ssd_gated_rmsnorm(ctypes.byref(d), _ptr(y), _ptr(z), _ptr(weight), float(eps), groups,
+                                            _ptr(out), s))
+
+
+def gated_rmsnorm(y, z, weight, eps: float = 1e-5, groups: int = 1, out=None):
+    """out = RMSNorm(y * silu(z)) * weight over `groups` channel groups of each
+    token (z None: y itself) through ssd_gated_rmsnorm; out=y normalises in
+    place. y, z [b,T,H,P]; weight [H*P] fp32."""
+    b, T, H, P = y.shape
+    d = make_dims(b, T, H, P, 16, 1, 32, "bf16" if y.dtype == torch.bfloat16 else "fp32", "fp32")
+    if weight.dtype != torch.float32 or weight.numel() != H * P:
+        raise ValueError(f"weight must be float32 [{H * P}]")
+    if z is not None and (z.shape != y.shape or z.dtype != y.dtype):
+        raise ValueError("z must have y's shape and type")
+    out = torch.empty_like(y) if out is None else out
+    ssd_gated_rmsnorm(d, y.contiguous(), None if z is None else z.contiguous(), weight.contiguous(), eps, groups, out)
+    return out
 
 
 def ssd_total_decay(d, dt, A, total, stream=None):

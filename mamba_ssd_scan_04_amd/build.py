@@ -30,7 +30,7 @@ FLAGS = [
     "-I", os.path.join(ROOT, "include"),
 ]
 SOURCES = ["ssd_api.hip", "chunk_cumsum.hip", "chunk_state.hip", "state_passing.hip", "chunk_scan.hip",
-           "ssd_step.hip", "shard.hip"]
+           "ssd_step.hip", "shard.hip", "norm.hip"]
 PEAK_SOURCES = ["peak_probe.hip"]
 
 

@@ -16,6 +16,8 @@ hipError_t launch_zero_fill(float* dst, int64_t n, hipStream_t s);
 hipError_t launch_step(const Params& p, int dtype, hipStream_t s);
 hipError_t launch_total_decay(const float* dt, const float* A, float* total, int64_t batch, int64_t T, int64_t H,
                               hipStream_t s);
+hipError_t launch_gated_rmsnorm(const void* y, const void* z, const float* w, float eps, int64_t rows, int64_t groups,
+                                int64_t cg, void* out, int dtype, hipStream_t s);
 hipError_t launch_fold(int64_t K, int64_t BH, int64_t NP, const float* totals, const float* finals, const float* init,
                        float* entering, hipStream_t s);
 

@@ -400,4 +400,21 @@ ssd_status ssd_fold_states(const ssd_dims* d, int64_t nshards, const float* tota
     return to_status(ssd::launch_fold(nshards, bh, np, totals, shard_finals, initial_state, entering, stream));
 }
 
+ssd_status ssd_gated_rmsnorm(const ssd_dims* d, const void* y, const void* z, const float* weight, float eps,
+                             int64_t groups, void* out, hipStream_t stream) {
+    if (!d) return SSD_ERR_NULL_POINTER;
+    if (d->batch < 0 || d->seqlen < 0 || d->nheads <= 0 || d->headdim <= 0 || groups <= 0)
+        return SSD_ERR_BAD_SHAPE;
+    const int64_t C = d->nheads * d->headdim;
+    if (C % groups != 0) return SSD_ERR_BAD_SHAPE;
+    if (d->dtype != SSD_F32 && d->dtype != SSD_BF16) return SSD_ERR_UNSUPPORTED;
+    if ((C / groups) % 8 != 0) return SSD_ERR_UNSUPPORTED;   // whole 8-channel pieces per group
+    const int64_t rows = d->batch * d->seqlen * groups;
+    if (rows == 0) return SSD_OK;
+    if (!y || !weight || !out) return SSD_ERR_NULL_POINTER;
+    if (!aligned16(y) || !aligned16(weight) || !aligned16(out) || (z && !aligned16(z))) return SSD_ERR_MISALIGNED;
+    if ((rows + 3) / 4 > (int64_t)INT32_MAX) return SSD_ERR_UNSUPPORTED;
+    return to_status(ssd::launch_gated_rmsnorm(y, z, weight, eps, rows, groups, C / groups, out, d->dtype, stream));
+}
+
 }  // extern "C"

@@ -225,7 +225,7 @@ def silu_gate(y, z):
 
 def gated_rmsnorm(y, z, weight, eps: float, groups: int = 1):
     """The normalisation after the gate in the Mamba-2 block ("Transformers are
-    SSMs", Knowl 6: Y_g = Y * SiLU(z), then GroupNorm or RMSNorm before the
+    SSMs", Knowl 6: Y_g = Y * SiLU(z), then a group or RMS norm before the
     output projection), fp64. Per token, the e*d = H*P channels of y [b,T,H,P]
     are cut into `groups` equal contiguous groups (1: plain RMSNorm over all
     channels; Knowl 8's GroupNorm with groups divisible by the TP degree), and

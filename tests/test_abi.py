@@ -259,3 +259,19 @@ def test_shard_entry_points_argument_errors(lib):
     assert lib.ssd_fold_states(P(d), 4, a, a, _fake(0x600008), a, None) == MISAL
     assert lib.ssd_fold_states(P(dims(nheads=0)), 4, a, a, None, a, None) == SHAPE
     assert lib.ssd_fold_states(P(dims(batch=0)), 4, None, None, None, None, None) == OK
+
+
+def test_gated_rmsnorm_argument_errors(lib):
+    P = ctypes.byref
+    a = _fake(0x700000)
+    d = dims()
+    f = lib.ssd_gated_rmsnorm
+    assert f(None, a, None, a, ctypes.c_float(1e-5), 1, a, None) == NULLP
+    assert f(P(d), None, None, a, ctypes.c_float(1e-5), 1, a, None) == NULLP
+    assert f(P(d), a, None, None, ctypes.c_float(1e-5), 1, a, None) == NULLP
+    assert f(P(d), a, None, a, ctypes.c_float(1e-5), 0, a, None) == SHAPE
+    assert f(P(d), a, None, a, ctypes.c_float(1e-5), 3, a, None) == SHAPE         # 3 does not divide 8 * 64
+    assert f(P(d), a, None, a, ctypes.c_float(1e-5), 128, a, None) == UNSUP       # 4 channels per group
+    assert f(P(d), a, _fake(0x700004), a, ctypes.c_float(1e-5), 1, a, None) == MISAL
+    assert f(P(dims(dtype=7)), a, None, a, ctypes.c_float(1e-5), 1, a, None) == UNSUP
+    assert f(P(dims(seqlen=0)), None, None, None, ctypes.c_float(1e-5), 1, None, None) == OK
