@@ -209,19 +209,16 @@ def cpu_baseline(inp, w, budget_s: float = 10.0) -> dict:
                       f"fp64 recurrence in {secs:.2f} s on {threads} threads; tokens/s = sequences*T/H/s"}
 
 
-def _counter_means(path: str, counter: str) -> dict:
-    """Per kernel name in a rocprofv3 counter_collection.csv: (mean counter
-    value, first dispatch id)."""
+def _counter_rows(path: str, counter: str) -> dict:
+    """Per kernel name in a rocprofv3 counter_collection.csv: the (dispatch id,
+    counter value) pairs, in dispatch order."""
     import csv
-    acc, first = {}, {}
+    rows = {}
     with open(path) as f:
         for r in csv.DictReader(f):
-            if r["Counter_Name"] != counter:
-                continue
-            name = r["Kernel_Name"]
-            acc.setdefault(name, []).append(float(r["Counter_Value"]))
-            first[name] = min(first.get(name, 1 << 62), int(r["Dispatch_Id"]))
-    return {k: (sum(v) / len(v), first[k]) for k, v in acc.items()}
+            if r["Counter_Name"] == counter:
+                rows.setdefault(r["Kernel_Name"], []).append((int(r["Dispatch_Id"]), float(r["Counter_Value"])))
+    return {k: sorted(v) for k, v in rows.items()}
 
 
 def record_traffic(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, workload, state_dtype) -> int:
@@ -235,31 +232,39 @@ def record_traffic(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, workload,
     launches them (the profiler prints some template names garbled): for each
     kernel, the first name is ssd_forward with the default state storage
     (bf16 for bf16 inputs), the second ssd_forward with the other storage;
-    the gated and packed-document instantiations come after both."""
+    the gated and then the packed-document instantiations come after both,
+    and after them the context-parallel share, whose launches are left out."""
     from mamba_ssd_scan_04_amd import inputs
     nbytes = 1 << 30
-    cf = _counter_means(cal_fetch_csv, "FETCH_SIZE")
-    cw = _counter_means(cal_write_csv, "WRITE_SIZE")
+    cf = _counter_rows(cal_fetch_csv, "FETCH_SIZE")
+    cw = _counter_rows(cal_write_csv, "WRITE_SIZE")
     copy = [k for k in cf if "copyBuffer" in k or "copy" in k.lower()]
     if not copy:
         print("no copy kernel in the calibration runs", file=sys.stderr)
         return 1
-    f_scale = nbytes / (cf[copy[0]][0] * 1024.0)
-    w_scale = nbytes / (cw[copy[0]][0] * 1024.0)
-    fe, wr = _counter_means(fetch_csv, "FETCH_SIZE"), _counter_means(write_csv, "WRITE_SIZE")
+    mean = lambda v: sum(x[1] for x in v) / len(v)
+    f_scale = nbytes / (mean(cf[copy[0]]) * 1024.0)
+    w_scale = nbytes / (mean(cw[copy[0]]) * 1024.0)
+    fe, wr = _counter_rows(fetch_csv, "FETCH_SIZE"), _counter_rows(write_csv, "WRITE_SIZE")
     w = inputs.WORKLOADS[workload]
     work = kernel_work(w, 2 if state_dtype == "bf16" else 4)
     default = "bf16" if w.dtype == "bf16" else "fp32"
     rank = 0 if state_dtype == default else 1
 
     for kern in KERNELS:
-        names = sorted((k for k in fe if kern + "_kernel" in k), key=lambda k: fe[k][1])
+        names = sorted((k for k in fe if kern + "_kernel" in k), key=lambda k: fe[k][0][0])
         if len(names) <= rank or names[rank] not in wr:
             print(f"{kern}: no dispatch name for {state_dtype} states among {names}", file=sys.stderr)
             continue
         name = names[rank]
-        rd = fe[name][0] * 1024.0 * f_scale
-        wb = wr[name][0] * 1024.0 * w_scale
+        # the packed-document instantiation is the last one launched at full
+        # size; later launches of the plain one are the context-parallel
+        # share's, on T/8 tokens, and are left out
+        last = names[-1] if len(names) > 2 else None
+        fsel = [x for x in fe[name] if last is None or x[0] < fe[last][0][0]]
+        wsel = [x for x in wr[name] if last is None or last not in wr or x[0] < wr[last][0][0]]
+        rd = mean(fsel) * 1024.0 * f_scale
+        wb = mean(wsel) * 1024.0 * w_scale
         rec = {"kernel": kern, "dispatch_name": name, "workload": workload, "state_dtype": state_dtype,
                "source_sha": source_sha(kern), "fetch_scale": round(f_scale, 4),
                "write_scale": round(w_scale, 4), "hbm_read_bytes_per_launch": int(rd),
