@@ -203,7 +203,24 @@ def cpu_baseline(inp, w, budget_s: float = 10.0) -> dict:
         secs, done, passes = secs + s2, done + d2, passes + 1
     tokens_equiv = done * w.seqlen / w.nheads
     what = (f"{passes} pass(es) over all {npairs}" if passes > 1 else f"{done}")
+    # the same on one thread, over one (batch, head) sequence, for the scaling
+    f1 = gen.to_float64({"x": inp["x"][:1, :, :1], "dt": inp["dt"][:1, :, :1], "A": inp["A"][:1],
+                         "B": inp["B"][:1, :, :1], "C": inp["C"][:1, :, :1], "D": inp["D"][:1]})
+    t1 = time.perf_counter()
+    oracle.recurrence(f1["x"], f1["dt"], f1["A"], f1["B"], f1["C"], f1["D"], nthreads=1)
+    t1 = time.perf_counter() - t1
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fc:
+            for line in fc:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": tokens_equiv / secs, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "seconds": round(secs, 3), "cpu_model": cpu_model,
+            "single_thread_tokens_per_s": round(w.seqlen / w.nheads / t1, 1),
             "sample": f"{what} whole (batch, head) sequences of {w.seqlen} tokens "
                       f"({done / w.nheads:.2f} batch elements' worth of the {w.nheads}-head layer in total), "
                       f"fp64 recurrence in {secs:.2f} s on {threads} threads; tokens/s = sequences*T/H/s"}
