@@ -425,6 +425,19 @@ def main() -> int:
     kms = {name: sum(events[k][i].elapsed_time(events[k][i + 1]) for k in range(args.steps)) / args.steps
            for i, name in enumerate(KERNELS)}
 
+    # the in-chunk prefix sums alone (ssd_chunk_cumsum, the stage that the
+    # forward forms inside the chunk-state launch), for its own HBM rate
+    for _ in range(args.warmup):
+        ssd.ssd_chunk_cumsum(d, g["dt"], g["A"], cs, sh)
+    ec0, ec1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ec0.record(stream)
+    for _ in range(args.steps):
+        ssd.ssd_chunk_cumsum(d, g["dt"], g["A"], cs, sh)
+    ec1.record(stream)
+    torch.cuda.synchronize()
+    cum_ms = ec0.elapsed_time(ec1) / args.steps
+
     # the other storage of the inter-chunk states, same inputs, for reference
     alt = None
     if w.dtype == "bf16":
@@ -572,6 +585,11 @@ def main() -> int:
                             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
                             "TFLOP/s": round(tfs, 2), "mfma_frac": round(tfs / peak_tf, 4),
                             "alg_bytes": work[name]["bytes"], "alg_flops": work[name]["flops"]}
+    cw = kernel_work(w, sbytes)["ssd_chunk_cumsum"]
+    cum_gbs = cw["bytes"] / (cum_ms * 1e-3) / 1e9
+    per_kernel["ssd_chunk_cumsum (standalone stage)"] = {
+        "ms": round(cum_ms, 5), "GB/s": round(cum_gbs, 1), "hbm_frac": round(cum_gbs / HBM_PEAK_GBS, 4),
+        "alg_bytes": cw["bytes"], "note": "formed inside the chunk-state launch in ssd_forward; timed alone here"}
     dom = max(KERNELS, key=lambda n: kms[n])
     traffic = measured_traffic(dom, w.name, args.state_dtype)
     roof = {"kernel": dom, "bound": "hbm", "achieved": per_kernel[dom]["GB/s"], "peak": HBM_PEAK_GBS,
