@@ -6,53 +6,40 @@
 // appendix B.3.2). The product of a chunk's decays is exp(cs_last).
 //
 // Every state element follows its own scalar recurrence, so the kernel is a
-// pure stream: each thread owns 8 consecutive elements of one (batch, head)
-// N x P state and walks the chunks in order, reading S_c and overwriting it in
-// place with h_c (the state entering chunk c). The running state stays in
-// fp32 registers whatever the storage type; the final state is transposed
-// through LDS.
+// pure stream: each thread owns E consecutive elements of one (batch, head)
+// N x P state (E = 8, or 4 when the states are too few to give the chip
+// enough wavefronts at 8) and walks the chunks in order, reading S_c and
+// overwriting it in place with h_c (the state entering chunk c). The running
+// state stays in fp32 registers whatever the storage type; the final state is
+// transposed through LDS.
 //
-// Grid: (P*N / 2048, head, batch), 256 threads.
+// Grid: (P*N / (256 E), head, batch), 256 threads.
 #include "kernels.hpp"
 
 namespace ssd {
 
-// 8 consecutive state elements <-> fp32
-template <typename ST> struct Oct;
-template <> struct Oct<float> {
-    typedef f32x8 raw;
-    static __device__ __forceinline__ raw load(const float* p) { return ldg8(p); }
-    static __device__ __forceinline__ f32x8 widen(const raw& r) { return r; }
-    static __device__ __forceinline__ void store(float* p, const f32x8& v) {
-        f32x4 lo, hi;
-        lo[0] = v[0]; lo[1] = v[1]; lo[2] = v[2]; lo[3] = v[3];
-        hi[0] = v[4]; hi[1] = v[5]; hi[2] = v[6]; hi[3] = v[7];
-        stg(reinterpret_cast<f32x4*>(p), lo);
-        stg(reinterpret_cast<f32x4*>(p + 4), hi);
+// E consecutive state elements (one vector load or store) <-> fp32
+template <typename ST, int E> struct Pack {
+    typedef ST raw __attribute__((ext_vector_type(E)));
+    static __device__ __forceinline__ raw load(const ST* p) {
+        return *(const __attribute__((address_space(1))) raw*)p;
     }
-};
-template <> struct Oct<bf16> {
-    typedef bf16x8 raw;
-    static __device__ __forceinline__ raw load(const bf16* p) { return ldg8(p); }
-    static __device__ __forceinline__ f32x8 widen(const raw& r) {
-        f32x8 v;
+    static __device__ __forceinline__ void widen(const raw& r, float (&v)[E]) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = to_f32(r[k]);
-        return v;
+        for (int k = 0; k < E; ++k) v[k] = to_f32(r[k]);
     }
-    static __device__ __forceinline__ void store(bf16* p, const f32x8& v) {
-        bf16x8 r;
+    static __device__ __forceinline__ void store(ST* p, const float (&v)[E]) {
+        raw r;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) r[k] = from_f32<bf16>(v[k]);
-        stg(reinterpret_cast<bf16x8*>(p), r);
+        for (int k = 0; k < E; ++k) r[k] = from_f32<ST>(v[k]);
+        *(__attribute__((address_space(1))) raw*)p = r;
     }
 };
 
 constexpr int kPassWin = 8;          // chunks whose loads are in flight together
 constexpr int kPassThreads = 256;
-constexpr int kPassElems = 8;        // consecutive state elements per thread
 
-// Each thread owns 8 consecutive elements of one (batch, head) [P][N] state.
+// Each thread owns E consecutive elements of one (batch, head) [P][N] state.
 // The chunk states are read in windows of 8 chunks, the next window's loads
 // issued before the current window is folded (h <- a h + S, storing h before
 // each fold), so up to 16 loads per thread are in flight.
@@ -60,10 +47,11 @@ constexpr int kPassElems = 8;        // consecutive state elements per thread
 // last token differs from that of the token before the chunk, or from the
 // first token's for chunk 0) passes no state on: its decay is 0 ("Transformers
 // are SSMs", Knowl 8).
-template <typename ST, bool VARLEN>
+template <typename ST, int E, bool VARLEN>
 __global__ __launch_bounds__(kPassThreads) void ssd_state_passing_kernel(Params p) {
+    constexpr int kPassElems = E;
     // the block's rows of the final state, row stride N + 1 (no bank conflicts
-    // on the transposed reads); at most 2048 / 16 = 128 rows
+    // on the transposed reads); at most 256 E / 16 rows
     __shared__ float fin_tile[kPassThreads * kPassElems + kPassThreads * kPassElems / 16];
     const int64_t H = p.nheads, P = p.headdim, N = p.dstate, Q = p.chunk, nc = p.nchunks;
     const int64_t PN = P * N;
@@ -74,18 +62,18 @@ __global__ __launch_bounds__(kPassThreads) void ssd_state_passing_kernel(Params 
     const float* lam = p.cs + (b * H + h) * nc * Q + (Q - 1);   // chunk c's total at lam[c*Q]
     ST* st = static_cast<ST*>(p.states) + (b * nc * H + h) * PN + (live ? e : 0);
     const int64_t cstride = H * PN;
-    using O = Oct<ST>;
+    using O = Pack<ST, E>;
 
     // the running state starts at h_0: zero, or the given initial state
     // ([N][P] per head, so element pr * N + n of the transposed state is
     // init[n * P + pr])
-    f32x8 run;
+    float run[E];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) run[k] = 0.0f;
+    for (int k = 0; k < E; ++k) run[k] = 0.0f;
     if (p.init_state && live) {
         const float* ini = p.init_state + (b * H + h) * PN;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
+        for (int k = 0; k < E; ++k) {
             const int64_t i = e + k, pr = i / N, n = i % N;
             run[k] = ini[n * P + pr];
         }
@@ -114,9 +102,10 @@ __global__ __launch_bounds__(kPassThreads) void ssd_state_passing_kernel(Params 
                 if (c0 + u < nc) {
                     O::store(st + (c0 + u) * cstride, run);
                     const float a = exp2f(acur[u] * kLog2e);
-                    const f32x8 sv = O::widen(cur[u]);
+                    float sv[E];
+                    O::widen(cur[u], sv);
 #pragma unroll
-                    for (int k = 0; k < 8; ++k) run[k] = a * run[k] + sv[k];
+                    for (int k = 0; k < E; ++k) run[k] = a * run[k] + sv[k];
                 }
             }
         }
@@ -132,7 +121,7 @@ __global__ __launch_bounds__(kPassThreads) void ssd_state_passing_kernel(Params 
     if (live) {
         const int64_t i0 = (int64_t)threadIdx.x * kPassElems;   // element i0 + k = r * N + n of the block
 #pragma unroll
-        for (int k = 0; k < 8; ++k) fin_tile[((i0 + k) / N) * (N + 1) + (i0 + k) % N] = run[k];
+        for (int k = 0; k < E; ++k) fin_tile[((i0 + k) / N) * (N + 1) + (i0 + k) % N] = run[k];
     }
     __syncthreads();
     const int64_t rows = (PN - e0) < (int64_t)kPassThreads * kPassElems ? (PN - e0) / N
@@ -147,20 +136,28 @@ __global__ __launch_bounds__(kPassThreads) void ssd_state_passing_kernel(Params 
     }
 }
 
-template <typename ST>
+template <typename ST, int E>
 static hipError_t launch_sp(const Params& p, hipStream_t s) {
     const int64_t PN = p.headdim * p.dstate;
-    const int64_t per_block = (int64_t)kPassThreads * kPassElems;
+    const int64_t per_block = (int64_t)kPassThreads * E;
     dim3 grid((unsigned)((PN + per_block - 1) / per_block), (unsigned)p.nheads, (unsigned)p.batch);
     if (p.seq_idx)
-        hipLaunchKernelGGL((ssd_state_passing_kernel<ST, true>), grid, dim3(kPassThreads), 0, s, p);
+        hipLaunchKernelGGL((ssd_state_passing_kernel<ST, E, true>), grid, dim3(kPassThreads), 0, s, p);
     else
-        hipLaunchKernelGGL((ssd_state_passing_kernel<ST, false>), grid, dim3(kPassThreads), 0, s, p);
+        hipLaunchKernelGGL((ssd_state_passing_kernel<ST, E, false>), grid, dim3(kPassThreads), 0, s, p);
     return hipGetLastError();
 }
 
+// 8 elements per thread, or 4 when 8 would leave fewer than 8 wavefronts per
+// compute unit (small states or few heads)
+template <typename ST>
+static hipError_t launch_sp_e(const Params& p, hipStream_t s) {
+    const int64_t waves8 = p.batch * p.nheads * p.headdim * p.dstate / 8 / 64;
+    return waves8 < 8 * (int64_t)device_cus() ? launch_sp<ST, 4>(p, s) : launch_sp<ST, 8>(p, s);
+}
+
 hipError_t launch_state_passing(const Params& p, int state_dtype, hipStream_t s) {
-    return state_dtype == 1 ? launch_sp<bf16>(p, s) : launch_sp<float>(p, s);
+    return state_dtype == 1 ? launch_sp_e<bf16>(p, s) : launch_sp_e<float>(p, s);
 }
 
 }  // namespace ssd
