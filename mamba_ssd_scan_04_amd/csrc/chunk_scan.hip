@@ -51,7 +51,7 @@ struct ScanCfg {
     static constexpr int KS = NT * 2;                          // k16 steps over n
     static constexpr int CBTILE = 2 * 64 * 8 * (int)sizeof(T);  // one 32x32 C B^T tile, lane-major
     __host__ __device__ static int xbytes(int Q) { return Q * XRC * 16; }
-    __host__ __device__ static int vbytes(int Q) { return 4 * Q * 4; }
+    __host__ __device__ static int vbytes(int Q) { return 3 * Q * 4; }
     // the off-diagonal C B^T tiles of all row tiles (kt < rt), when kept in LDS
     __host__ __device__ static int cbbytes(int Q) { return (Q / 32) * (Q / 32 - 1) / 2 * CBTILE; }
     // bytes of LDS with nbx x buffers, nbh h_c buffers, C B^T in LDS or not,
@@ -154,16 +154,13 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
     };
     float vcs = 0.0f, vcr = 0.0f, vdt = 0.0f;   // thread i holds token i of the next head
     // packed documents: thread i < Q holds the id of token i (clamped to the
-    // chunk) and whether it is in the document of the token before the chunk
-    // (the first token's for chunk 0, whose carried state is the initial one)
-    int vsq = 0;
-    bool vok = true;
+    // chunk); sprev is the id of the token before the chunk (the first token's
+    // for chunk 0, whose carried state is the initial one)
+    int vsq = 0, sprev = 0;
     if constexpr (VARLEN) {
         const int* sq = p.seq_idx + b * T_;
-        if ((int)threadIdx.x < Q) {
-            vsq = sq[t0 + min((int)threadIdx.x, qc - 1)];
-            vok = vsq == sq[c > 0 ? t0 - 1 : 0];
-        }
+        sprev = sq[c > 0 ? t0 - 1 : 0];
+        if ((int)threadIdx.x < Q) vsq = sq[t0 + min((int)threadIdx.x, qc - 1)];
     }
     auto load_vec = [&](int hh) {
         const int i = threadIdx.x;
@@ -175,18 +172,16 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
         }
     };
     // per-head vectors in LDS, token i of the chunk (log2 units: c2 = cs log2 e):
-    //   [0, Q)   c2_i
-    //   [Q, 2Q)  2^c2_i                          (carried-state row scale)
-    //   [2Q,3Q)  2^(c2_r - c2_i) dt_i, r = the last token of i's 32-token tile
-    //   [3Q,4Q)  dt_i                            (0 past the chunk's end)
+    //   [0, Q)   c2_i                            (2^c2_j is the carried-state row scale)
+    //   [Q, 2Q)  2^(c2_r - c2_i) dt_i, r = the last token of i's 32-token tile
+    //   [2Q,3Q)  dt_i                            (0 past the chunk's end)
     auto store_vec = [&](float* v) {
         const int i = threadIdx.x;
         if (i < Q) {
             const float c2 = vcs * kLog2e, c2r = vcr * kLog2e;
             v[i] = c2;
-            v[Q + i] = vok ? exp2f(c2) : 0.0f;
-            v[2 * Q + i] = exp2f(c2r - c2) * vdt;
-            v[3 * Q + i] = vdt;
+            v[Q + i] = exp2f(c2r - c2) * vdt;
+            v[2 * Q + i] = vdt;
         }
     };
 
@@ -355,9 +350,8 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
         }
         bool stored_all = true;
         if (active) {
-            const float* ecs = c2v + Q;
-            const float* uv = c2v + 2 * Q;
-            const float* dtv = c2v + 3 * Q;
+            const float* uv = c2v + Q;
+            const float* dtv = c2v + 2 * Q;
             int jl = rt * 32 + l32, qch = qc;
             asm volatile("" : "+v"(jl), "+v"(qch));    // keep per-element compares in the loop
             // The products are formed transposed, Y^T = X^T M^T (+ h^T C^T): the
@@ -388,7 +382,10 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
                 const float zf = to_f32(zv);
                 return yv * (zf * __builtin_amdgcn_rcpf(1.0f + fast_exp2(-zf * kLog2e)));
             };
-            const float ej = ecs[jl];
+            // the carried state reaches row j scaled by 2^c2_j (not at all
+            // when a document starts inside the chunk at or before j)
+            float ej = exp2f(c2j);
+            if constexpr (VARLEN) ej = sqj == sprev ? ej : 0.0f;
 
             // stage k < rt: off-diagonal key tile k; k == rt: the diagonal tile.
             // Every stage issues the same LDS reads whatever k is (addresses are
@@ -682,7 +679,7 @@ hipError_t launch_chunk_scan(const Params& p, int dtype, int state_dtype, hipStr
 int chunk_scan_lds_bytes(int dtype, int state_dtype, int64_t P, int64_t N, int64_t Q) {
     const int esz = dtype == 1 ? 2 : 4, ssz = state_dtype == 1 ? 2 : 4;
     const int pp = (int)((P + 31) / 32) * 32, np = (int)((N + 31) / 32) * 32;
-    return (int)Q * pp * esz + pp * np * ssz + 2 * 4 * (int)Q * 4;
+    return (int)Q * pp * esz + pp * np * ssz + 2 * 3 * (int)Q * 4;
 }
 
 }  // namespace ssd
