@@ -12,6 +12,16 @@
  * recurrence on N x P chunk states between chunks. Heads of one group share
  * B and C (Knowl 7, the multi-input / grouped-input patterns).
  *
+ * Entry points: ssd_forward (the whole transform) and its stages
+ * (ssd_chunk_cumsum, ssd_chunk_state, ssd_chunk_cumsum_state,
+ * ssd_state_passing, ssd_chunk_scan); from a given initial state
+ * (ssd_forward_init, ssd_state_passing_init, ssd_chunk_scan_init); with the
+ * block's output gate (ssd_forward_gated) and the norm after it
+ * (ssd_gated_rmsnorm); over rows packing several documents
+ * (ssd_forward_varlen); one decoding token (ssd_step); the shard chain of
+ * sequence parallelism (ssd_total_decay, ssd_fold_states); and sizing,
+ * checking and status helpers.
+ *
  * Conventions for every entry point:
  *  - All tensor pointers are DEVICE pointers to contiguous row-major arrays,
  *    16-byte aligned. The caller owns every buffer; the library never
