@@ -83,3 +83,29 @@ def test_fullsize_eight_shards_sampled(name):
     ey, ef = oracle.rel_err(np.stack(ys), np.stack(yr)), oracle.rel_err(np.stack(fs), np.stack(fr))
     say(f"  err_y={ey:.3e} err_final={ef:.3e}")
     assert ey <= TOL[w.dtype] and ef <= TOL[w.dtype]
+
+
+def test_fold_chain_against_fp64():
+    """ssd_fold_states alone: H_0 = init (or 0), H_{k+1} = exp(L_k) H_k + F_k,
+    against the same chain in fp64 on the same bits, for K = 0, 1 and 5."""
+    g = torch.Generator().manual_seed(54)
+    b, H, N, P = 2, 3, 16, 32
+    d = ssd.make_dims(b, 64, H, P, N, 1, 32, "fp32", "fp32")
+    for K in (0, 1, 5):
+        for with_init in (False, True):
+            tot = -torch.rand((K, b, H), generator=g) * 3.0
+            fin = torch.randn((K, b, H, N, P), generator=g)
+            ini = torch.randn((b, H, N, P), generator=g) if with_init else None
+            ent = torch.full((K + 1, b, H, N, P), float("nan"), device="cuda")
+            ssd.ssd_fold_states(d, K, tot.cuda() if K else None, fin.cuda() if K else None,
+                                None if ini is None else ini.cuda(), ent)
+            torch.cuda.synchronize()
+            ref = np.zeros((K + 1, b, H, N, P))
+            run = np.zeros((b, H, N, P)) if ini is None else ini.numpy().astype(np.float64)
+            for k in range(K):
+                ref[k] = run
+                run = np.exp(tot[k].numpy().astype(np.float64))[:, :, None, None] * run + fin[k].numpy()
+            ref[K] = run
+            got = ent.cpu().numpy().astype(np.float64)
+            assert np.all(np.isfinite(got))
+            assert oracle.rel_err(got, ref) < 1e-5, (K, with_init)
