@@ -163,7 +163,7 @@ def cpu_baseline(inp, w, budget_s: float = 10.0) -> dict:
     import oracle
     from mamba_ssd_scan_04_amd import inputs as gen
 
-    threads = max(1, min(16, oracle.default_threads()))
+    threads = max(1, oracle.default_threads())   # every core in this process's affinity mask
     hpg = w.nheads // w.ngroups
 
     def run(npairs):
@@ -219,6 +219,7 @@ def cpu_baseline(inp, w, budget_s: float = 10.0) -> dict:
     except OSError:
         pass
     return {"value": tokens_equiv / secs, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "host_cpus": os.cpu_count(), "affinity_cpus": oracle.default_threads(),
             "seconds": round(secs, 3), "cpu_model": cpu_model,
             "single_thread_tokens_per_s": round(w.seqlen / w.nheads / t1, 1),
             "sample": f"{what} whole (batch, head) sequences of {w.seqlen} tokens "
@@ -316,7 +317,10 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=100)   # ~40 ms: clocks settle before timing
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--settle-ms", type=float, default=500.0,
+                    help="untimed forward calls for this long before the warmup steps, so that the GPU "
+                         "clocks have left their idle state whatever --warmup is")
     ap.add_argument("--workload", default="m2p7")
     ap.add_argument("--state-dtype", default=None, choices=["fp32", "bf16"],
                     help="storage of the inter-chunk states (default: bf16 for bf16 inputs); the "
@@ -381,6 +385,17 @@ def main() -> int:
     def forward():
         ssd.ssd_forward(d, g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], y, final, ws, ws.numel(), sh)
 
+    # settle: untimed calls until the clocks have ramped up from idle (input
+    # generation on the host leaves the GPU idle for seconds); then the warmup
+    # steps, then the timed steps, which run exactly what the warmup ran
+    torch.cuda.synchronize()
+    settle_calls, ts0 = 0, time.perf_counter()
+    while (time.perf_counter() - ts0) * 1e3 < args.settle_ms:
+        for _ in range(20):
+            forward()
+        torch.cuda.synchronize()
+        settle_calls += 20
+    settle_ms = (time.perf_counter() - ts0) * 1e3
     # the step that is timed: one ssd_forward call
     for _ in range(args.warmup):
         forward()
@@ -607,6 +622,8 @@ def main() -> int:
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "settle": {"ms": round(settle_ms, 1), "calls": settle_calls,
+                   "what": "untimed ssd_forward calls before the warmup steps, so that the clocks leave idle"},
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": f"{w.name}: Mamba-2 2.7B-layer SSD shape" if w.name == "m2p7" else w.name,

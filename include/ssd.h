@@ -108,7 +108,7 @@ ssd_status ssd_stage_sizes(const ssd_dims* d, size_t* cs_bytes, size_t* states_b
 
 /*
  * Full forward: Knowl 2's inputs X, A, B, C and chunk size Q, its outputs Y and
- * h_final ("Input"/"Output" lines of the algorithm), with the per-head
+ * h_final (the algorithm's inputs and outputs), with the per-head
  * discretisation dt, A and the skip term D. Enqueues, in order,
  * ssd_chunk_cumsum_state (stages 1 and 2 in one launch), ssd_state_passing
  * and ssd_chunk_scan; the result is bitwise that of the four stage entry
@@ -250,9 +250,9 @@ ssd_status ssd_step(const ssd_dims* d, const void* x, const float* dt, const flo
                     const void* C, const float* D, float* state, void* y, hipStream_t stream);
 
 /*
- * Stage 1 (Knowl 2, "intra-chunk cumulative products of A", taken in log
- * space): cs[b,h,c,j] = sum_{s=0..j} dt[b,cQ+s,h] * A[h], an inclusive prefix
- * sum per chunk, so exp(cs) is the cumulative product of a. Positions past the
+ * Stage 1 (Knowl 2, first step: the running products of the decays inside
+ * each chunk, taken in log space): cs[b,h,c,j] = sum_{s=0..j} dt[b,cQ+s,h] * A[h],
+ * an inclusive prefix sum per chunk, so exp(cs) is the cumulative product of a. Positions past the
  * end of a short last chunk repeat its last value (padding tokens have dt = 0).
  *   dt [b,T,H], A [H] in; cs [b,H,nc,Q] fp32 out.
  */
@@ -260,7 +260,8 @@ ssd_status ssd_chunk_cumsum(const ssd_dims* d, const float* dt, const float* A, 
                             hipStream_t stream);
 
 /*
- * Stage 2 (Knowl 2, "right factor chunk state" S = B^T (decayed X)):
+ * Stage 2 (Knowl 2, second step: the chunk state S, B^T times the inputs
+ * decayed to the chunk's end):
  *   states[b,c,h,p,n] = sum_j B[b,cQ+j,g,n] * exp(cs_last - cs_j) * dt[b,cQ+j,h] * x[b,cQ+j,h,p]
  * where cs_last is the chunk's last cs value: each token is decayed to the end
  * of its chunk. bf16 MFMA (fp32 MFMA for fp32 inputs), fp32 accumulation.

@@ -112,6 +112,92 @@ def _ptr(t) -> int | None:
     return t.data_ptr()
 
 
+# ---- argument checks ------------------------------------------------------------
+#
+# The C ABI receives bare pointers and cannot see sizes, types or devices, so
+# the binding checks every tensor against the dims before a call: a wrong type
+# (dt in bf16 read as fp32), a short buffer or a host tensor would otherwise be
+# read or written out of bounds by the kernels. None (NULL) and raw integer
+# addresses are passed through unchecked; the C ABI rejects a NULL it needs.
+
+def _torch_dtype(code: int) -> torch.dtype:
+    return torch.bfloat16 if code == SSD_BF16 else torch.float32
+
+
+def _expect_type(name: str, t, shape, dtype):
+    if t is None or isinstance(t, int):
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(int(v) for v in shape):
+        raise ValueError(f"{name} must have shape {tuple(int(v) for v in shape)}, got {tuple(t.shape)}")
+
+
+def _expect_device(name: str, t, device=None):
+    if not isinstance(t, torch.Tensor):
+        return
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a CUDA device, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, other arguments on {device}")
+
+
+def _expect_all(items):
+    """items: (name, tensor, shape, dtype). Types and shapes of all, then devices."""
+    for name, t, shape, dtype in items:
+        _expect_type(name, t, shape, dtype)
+    dev = _device_of(*(it[1] for it in items))
+    for name, t, _, _ in items:
+        _expect_device(name, t, dev)
+
+
+def _expect(name: str, t, shape, dtype, device=None):
+    _expect_type(name, t, shape, dtype)
+    _expect_device(name, t, device)
+
+
+def _device_of(*ts):
+    for t in ts:
+        if isinstance(t, torch.Tensor):
+            return t.device
+    return None
+
+
+def _shapes(d: "SsdDims") -> dict:
+    b, T, H, P, N, G = d.batch, d.seqlen, d.nheads, d.headdim, d.dstate, d.ngroups
+    return {"x": (b, T, H, P), "dt": (b, T, H), "A": (H,), "D": (H,), "B": (b, T, G, N),
+            "state": (b, H, N, P), "seq_idx": (b, T), "cs": (b, H, d.nchunks, d.chunk_size),
+            "states": (b, d.nchunks, H, P, N)}
+
+
+def _check_io(d: "SsdDims", **args):
+    """Check the named tensors of one call against d (names as in include/ssd.h)."""
+    sh = _shapes(d)
+    xt, st = _torch_dtype(d.dtype), _torch_dtype(d.state_dtype)
+    spec = {"x": (sh["x"], xt), "y": (sh["x"], xt), "z": (sh["x"], xt), "out": (sh["x"], xt),
+            "dt": (sh["dt"], torch.float32), "A": (sh["A"], torch.float32), "D": (sh["D"], torch.float32),
+            "B": (sh["B"], xt), "C": (sh["B"], xt),
+            "final_state": (sh["state"], torch.float32), "initial_state": (sh["state"], torch.float32),
+            "state": (sh["state"], torch.float32),
+            "seq_idx": (sh["seq_idx"], torch.int32), "cs": (sh["cs"], torch.float32),
+            "states": (sh["states"], st)}
+    _expect_all([(name, t) + spec[name] for name, t in args.items()])
+
+
+def _check_workspace(workspace, workspace_bytes: int, device=None):
+    if workspace is None or isinstance(workspace, int):
+        return
+    if not isinstance(workspace, torch.Tensor) or workspace.device.type != "cuda":
+        raise ValueError("workspace must be a CUDA tensor")
+    if device is not None and workspace.device != device:
+        raise ValueError(f"workspace is on {workspace.device}, other arguments on {device}")
+    have = workspace.numel() * workspace.element_size()
+    if workspace_bytes > have:
+        raise ValueError(f"workspace_bytes ({workspace_bytes}) exceeds the workspace tensor ({have} bytes)")
+
+
 def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
@@ -125,10 +211,16 @@ def make_dims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_size, dtype
 
 
 def dims_of(x: torch.Tensor, B: torch.Tensor, chunk_size: int, state_dtype="fp32") -> SsdDims:
+    if x.dim() != 4 or B.dim() != 4:
+        raise ValueError(f"x must be [b,T,H,P] and B [b,T,G,N], got {tuple(x.shape)} and {tuple(B.shape)}")
     b, T, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
     if x.dtype not in _DTYPE_CODE:
         raise TypeError(f"x must be float32 or bfloat16, got {x.dtype}")
+    if B.dtype != x.dtype:
+        raise TypeError(f"B must have x's type {x.dtype}, got {B.dtype}")
+    if tuple(B.shape[:2]) != (b, T):
+        raise ValueError(f"B must be [{b},{T},G,N], got {tuple(B.shape)}")
     return make_dims(b, T, H, P, N, G, chunk_size, x.dtype, state_dtype)
 
 
@@ -157,6 +249,8 @@ def ssd_stage_sizes(d: SsdDims) -> tuple[int, int]:
 
 
 def ssd_forward(d, x, dt, A, B, C, D, y, final_state, workspace, workspace_bytes, stream=None):
+    _check_io(d, x=x, dt=dt, A=A, B=B, C=C, D=D, y=y, final_state=final_state)
+    _check_workspace(workspace, workspace_bytes, _device_of(x))
     s = _stream(x.device) if stream is None else stream
     _check(load_library().ssd_forward(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
                                       _ptr(C), _ptr(D), _ptr(y), _ptr(final_state),
@@ -165,6 +259,8 @@ def ssd_forward(d, x, dt, A, B, C, D, y, final_state, workspace, workspace_bytes
 
 def ssd_forward_init(d, x, dt, A, B, C, D, initial_state, y, final_state, workspace, workspace_bytes,
                      stream=None):
+    _check_io(d, x=x, dt=dt, A=A, B=B, C=C, D=D, initial_state=initial_state, y=y, final_state=final_state)
+    _check_workspace(workspace, workspace_bytes, _device_of(final_state))
     s = _stream(final_state.device) if stream is None else stream
     _check(load_library().ssd_forward_init(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
                                            _ptr(C), _ptr(D), _ptr(initial_state), _ptr(y),
@@ -173,6 +269,8 @@ def ssd_forward_init(d, x, dt, A, B, C, D, initial_state, y, final_state, worksp
 
 def ssd_forward_gated(d, x, dt, A, B, C, D, initial_state, z, y, final_state, workspace, workspace_bytes,
                       stream=None):
+    _check_io(d, x=x, dt=dt, A=A, B=B, C=C, D=D, initial_state=initial_state, z=z, y=y, final_state=final_state)
+    _check_workspace(workspace, workspace_bytes, _device_of(final_state))
     s = _stream(final_state.device) if stream is None else stream
     _check(load_library().ssd_forward_gated(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
                                             _ptr(C), _ptr(D), _ptr(initial_state), _ptr(z), _ptr(y),
@@ -181,6 +279,9 @@ def ssd_forward_gated(d, x, dt, A, B, C, D, initial_state, z, y, final_state, wo
 
 def ssd_forward_varlen(d, x, dt, A, B, C, D, initial_state, seq_idx, y, final_state, workspace,
                        workspace_bytes, stream=None):
+    _check_io(d, x=x, dt=dt, A=A, B=B, C=C, D=D, initial_state=initial_state, seq_idx=seq_idx, y=y,
+              final_state=final_state)
+    _check_workspace(workspace, workspace_bytes, _device_of(final_state))
     s = _stream(final_state.device) if stream is None else stream
     _check(load_library().ssd_forward_varlen(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
                                              _ptr(C), _ptr(D), _ptr(initial_state), _ptr(seq_idx), _ptr(y),
@@ -188,6 +289,9 @@ def ssd_forward_varlen(d, x, dt, A, B, C, D, initial_state, seq_idx, y, final_st
 
 
 def ssd_gated_rmsnorm(d, y, z, weight, eps, groups, out, stream=None):
+    xt, shx = _torch_dtype(d.dtype), _shapes(d)["x"]
+    _expect_all([("y", y, shx, xt), ("z", z, shx, xt), ("out", out, shx, xt),
+                 ("weight", weight, (d.nheads * d.headdim,), torch.float32)])
     s = _stream(out.device) if stream is None else stream
     _check(load_library().ssd_gated_rmsnorm(ctypes.byref(d), _ptr(y), _ptr(z), _ptr(weight), float(eps), groups,
                                             _ptr(out), s))
@@ -209,58 +313,79 @@ def gated_rmsnorm(y, z, weight, eps: float = 1e-5, groups: int = 1, out=None):
 
 
 def ssd_total_decay(d, dt, A, total, stream=None):
+    sh = _shapes(d)
+    _expect_all([("dt", dt, sh["dt"], torch.float32), ("A", A, sh["A"], torch.float32),
+                 ("total", total, (d.batch, d.nheads), torch.float32)])
     s = _stream(total.device) if stream is None else stream
     _check(load_library().ssd_total_decay(ctypes.byref(d), _ptr(dt), _ptr(A), _ptr(total), s))
 
 
 def ssd_fold_states(d, nshards, totals, shard_finals, initial_state, entering, stream=None):
+    sh = _shapes(d)["state"]
+    _expect_all([("totals", totals, (nshards, d.batch, d.nheads), torch.float32),
+                 ("shard_finals", shard_finals, (nshards,) + sh, torch.float32),
+                 ("initial_state", initial_state, sh, torch.float32),
+                 ("entering", entering, (nshards + 1,) + sh, torch.float32)])
     s = _stream(entering.device) if stream is None else stream
     _check(load_library().ssd_fold_states(ctypes.byref(d), nshards, _ptr(totals), _ptr(shard_finals),
                                           _ptr(initial_state), _ptr(entering), s))
 
 
 def ssd_chunk_cumsum(d, dt, A, cs, stream=None):
+    _check_io(d, dt=dt, A=A, cs=cs)
     s = _stream(dt.device) if stream is None else stream
     _check(load_library().ssd_chunk_cumsum(ctypes.byref(d), _ptr(dt), _ptr(A), _ptr(cs), s))
 
 
 def ssd_chunk_state(d, x, dt, B, cs, states, stream=None):
+    _check_io(d, x=x, dt=dt, B=B, cs=cs, states=states)
     s = _stream(x.device) if stream is None else stream
     _check(load_library().ssd_chunk_state(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(B), _ptr(cs),
                                           _ptr(states), s))
 
 
 def ssd_chunk_cumsum_state(d, x, dt, A, B, cs, states, stream=None):
+    _check_io(d, x=x, dt=dt, A=A, B=B, cs=cs, states=states)
     s = _stream(x.device) if stream is None else stream
     _check(load_library().ssd_chunk_cumsum_state(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
                                                  _ptr(cs), _ptr(states), s))
 
 
 def ssd_state_passing(d, cs, states, final_state, stream=None):
+    _check_io(d, cs=cs, states=states, final_state=final_state)
     s = _stream(final_state.device) if stream is None else stream
     _check(load_library().ssd_state_passing(ctypes.byref(d), _ptr(cs), _ptr(states),
                                             _ptr(final_state), s))
 
 
 def ssd_state_passing_init(d, cs, states, initial_state, final_state, stream=None):
+    _check_io(d, cs=cs, states=states, initial_state=initial_state, final_state=final_state)
     s = _stream(final_state.device) if stream is None else stream
     _check(load_library().ssd_state_passing_init(ctypes.byref(d), _ptr(cs), _ptr(states),
                                                  _ptr(initial_state), _ptr(final_state), s))
 
 
 def ssd_chunk_scan_init(d, x, dt, B, C, D, cs, states, y, stream=None):
+    _check_io(d, x=x, dt=dt, B=B, C=C, D=D, cs=cs, states=states, y=y)
     s = _stream(x.device) if stream is None else stream
     _check(load_library().ssd_chunk_scan_init(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(B), _ptr(C),
                                               _ptr(D), _ptr(cs), _ptr(states), _ptr(y), s))
 
 
 def ssd_chunk_scan(d, x, dt, B, C, D, cs, states, y, stream=None):
+    _check_io(d, x=x, dt=dt, B=B, C=C, D=D, cs=cs, states=states, y=y)
     s = _stream(x.device) if stream is None else stream
     _check(load_library().ssd_chunk_scan(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(B), _ptr(C),
                                          _ptr(D), _ptr(cs), _ptr(states), _ptr(y), s))
 
 
 def ssd_step(d, x, dt, A, B, C, D, state, y, stream=None):
+    b, H, P, N, G = d.batch, d.nheads, d.headdim, d.dstate, d.ngroups
+    xt = _torch_dtype(d.dtype)
+    _expect_all([("x", x, (b, H, P), xt), ("dt", dt, (b, H), torch.float32),
+                 ("A", A, (H,), torch.float32), ("B", B, (b, G, N), xt),
+                 ("C", C, (b, G, N), xt), ("D", D, (H,), torch.float32),
+                 ("state", state, (b, H, N, P), torch.float32), ("y", y, (b, H, P), xt)])
     s = _stream(state.device) if stream is None else stream
     _check(load_library().ssd_step(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
                                    _ptr(D), _ptr(state), _ptr(y), s))
@@ -292,6 +417,7 @@ def forward(x, dt, A, B, C, D, chunk_size: int, state_dtype: str | None = None, 
         state_dtype = "bf16" if x.dtype == torch.bfloat16 else "fp32"
     d = dims_of(x, B, chunk_size, state_dtype)
     _check(ssd_check_dims(d))
+    _check_io(d, x=x, dt=dt, A=A, B=B, C=C, D=D, initial_state=initial_state, z=z, seq_idx=seq_idx)
     y = torch.empty_like(x)
     final = torch.empty((d.batch, d.nheads, d.dstate, d.headdim), dtype=torch.float32, device=x.device)
     if workspace is None:
@@ -357,8 +483,6 @@ def step(x, dt, A, B, C, D, state):
     G, N = B.shape[1], B.shape[2]
     if x.dtype not in _DTYPE_CODE:
         raise TypeError(f"x must be float32 or bfloat16, got {x.dtype}")
-    if state.dtype != torch.float32 or tuple(state.shape) != (b, H, N, P):
-        raise ValueError(f"state must be float32 {(b, H, N, P)}")
     d = make_dims(b, 1, H, P, N, G, 32, x.dtype, "fp32")
     y = torch.empty_like(x)
     ssd_step(d, x, dt, A, B, C, D, state, y)
@@ -371,6 +495,7 @@ def stages(x, dt, A, B, C, D, chunk_size: int, state_dtype: str = "fp32"):
     layout: state entering each chunk), final [b,H,N,P], y."""
     d = dims_of(x, B, chunk_size, state_dtype)
     _check(ssd_check_dims(d))
+    _check_io(d, x=x, dt=dt, A=A, B=B, C=C, D=D)
     dev = x.device
     b, H, P, N, nc, Q = d.batch, d.nheads, d.headdim, d.dstate, d.nchunks, d.chunk_size
     cs = torch.empty((b, H, nc, Q), dtype=torch.float32, device=dev)

@@ -2,7 +2,8 @@
 
     python -m mamba_ssd_scan_04_amd.build
 
-Each .hip file is compiled to an object in parallel, then linked into
+Each .hip file (the chunk-scan unit once per instantiation set) is compiled to
+an object in parallel, then linked into
 mamba_ssd_scan_04_amd/libssd.so. The attainable-peak probes (an MFMA loop and
 a streaming copy, used by the benchmark only) go into libssd_peak.so.
 """
@@ -29,14 +30,21 @@ FLAGS = [
     "-Wall", "-Wno-unused-command-line-argument",
     "-I", os.path.join(ROOT, "include"),
 ]
-SOURCES = ["ssd_api.hip", "chunk_cumsum.hip", "chunk_state.hip", "state_passing.hip", "chunk_scan.hip",
-           "ssd_step.hip", "shard.hip", "norm.hip"]
-PEAK_SOURCES = ["peak_probe.hip"]
+# (source, object name, extra defines). The chunk-scan kernel is compiled once
+# per (input type, state type, variant) from chunk_scan_inst.hip, so that its
+# many template instantiations build in parallel.
+_SC_UNITS = [("chunk_scan_inst.hip", f"chunk_scan_{x}_{s}_{v}", [f"-DSSD_SC_X={x}", f"-DSSD_SC_S={s}", f"-DSSD_SC_V={v}"])
+             for x, s in (("bf16", "bf16"), ("bf16", "f32"), ("f32", "f32")) for v in (0, 1, 2)]
+SOURCES = [(f, os.path.splitext(f)[0], []) for f in
+           ("ssd_api.hip", "chunk_cumsum.hip", "chunk_state.hip", "state_passing.hip", "chunk_scan.hip",
+            "ssd_step.hip", "shard.hip", "norm.hip")] + _SC_UNITS
+PEAK_SOURCES = [("peak_probe.hip", "peak_probe", [])]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(unit) -> str:
+    src, name, defs = unit
+    obj = os.path.join(BUILD_DIR, name + ".o")
+    cmd = [HIPCC, *FLAGS, *defs, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
@@ -54,11 +62,14 @@ def _link(objs, out: str) -> None:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
-    srcs = SOURCES + PEAK_SOURCES
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = dict(zip(srcs, ex.map(_compile, srcs)))
-    _link([objs[s] for s in SOURCES], OUT)
-    _link([objs[s] for s in PEAK_SOURCES], PEAK_OUT)
+    units = SOURCES + PEAK_SOURCES
+    jobs = int(os.environ.get("SSD_BUILD_JOBS", str(min(8, os.cpu_count() or 1))))
+    # the chunk-scan units first: they take longest
+    order = sorted(units, key=lambda u: u[0] != "chunk_scan_inst.hip")
+    with concurrent.futures.ThreadPoolExecutor(max_workers=max(1, min(jobs, len(units)))) as ex:
+        objs = dict(zip((u[1] for u in order), ex.map(_compile, order)))
+    _link([objs[u[1]] for u in SOURCES], OUT)
+    _link([objs[u[1]] for u in PEAK_SOURCES], PEAK_OUT)
     if verbose:
         print(f"built {OUT} and {PEAK_OUT}")
     return OUT

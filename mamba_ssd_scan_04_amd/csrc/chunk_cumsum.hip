@@ -1,9 +1,9 @@
 // ssd_chunk_cumsum: in-chunk cumulative decay in log space.
 //
-// "Transformers are SSMs" (chapterpal summary), Knowl 2, step "compute
-// intra-chunk cumulative products of A". With a_t = exp(dt_t * A_h) the
-// cumulative product over a chunk is exp of the inclusive prefix sum of
-// dt_t * A_h; keeping the sum (not the product) avoids fp32 underflow within a
+// "Transformers are SSMs" (chapterpal summary), Knowl 2, first step of the
+// block decomposition: the running products of the decays inside each chunk.
+// With a_t = exp(dt_t * A_h) the cumulative product over a chunk is exp of the
+// inclusive prefix sum of dt_t * A_h; keeping the sum (not the product) avoids fp32 underflow within a
 // chunk. The prefix is a parallel (Hillis-Steele) scan across a wavefront,
 // the parallel associative scan of the paper's appendix B.2.2.
 //

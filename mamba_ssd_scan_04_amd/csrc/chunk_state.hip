@@ -1,7 +1,8 @@
 // ssd_chunk_state: the right-factor state of every chunk.
 //
-// "Transformers are SSMs" (chapterpal summary), Knowl 2, step "compute right
-// factor chunk state S = B^T (decayed X)". "Decayed" is read as: token j of
+// "Transformers are SSMs" (chapterpal summary), Knowl 2, second step of the
+// block decomposition: each chunk's state, B^T applied to the inputs after
+// their decay to the chunk's end. That decay is read as: token j of
 // the chunk is scaled by the decay from j to the chunk's end,
 // exp(cs_last - cs_j) = a_{j+1} ... a_{last} (so that chaining chunk states
 // reproduces the recurrence exactly), and by its step dt_j (the input term of

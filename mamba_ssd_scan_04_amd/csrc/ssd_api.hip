@@ -2,6 +2,8 @@
 // layout and the launch order of the four kernels. No allocation, no state.
 #include <stdint.h>
 
+#include <atomic>
+
 #include "ssd.h"
 #include "kernels.hpp"
 
@@ -11,15 +13,16 @@ int chunk_scan_lds_bytes(int dtype, int state_dtype, int64_t P, int64_t N, int64
 
 namespace ssd {
 int device_cus() {
-    static int cache[64] = {0};
+    // per-device cache; threads that race on a first call store the same value
+    static std::atomic<int> cache[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cache[dev] == 0) {
-        int n = 0;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cache[dev] = n;
+        cache[dev].store(n, std::memory_order_relaxed);
     }
-    return cache[dev];
+    return n;
 }
 }  // namespace ssd
 
@@ -81,7 +84,8 @@ const char* ssd_status_string(ssd_status s) {
         case SSD_ERR_UNSUPPORTED:
             return "unsupported configuration: headdim in {16,32,64,128}, dstate in {16,32,64,128,256}, "
                    "chunk_size in {32,64,128,256}, dtype fp32/bf16, bf16 states only with bf16 inputs, "
-                   "and the chunk scan's x and state tiles must fit in LDS (Q*P*esize + P*N*ssize <= ~156 KB)";
+                   "the chunk scan's x and state tiles must fit in LDS (Q*P*esize + P*N*ssize <= ~156 KB), "
+                   "and one chunk's rows must span less than 2^31 bytes (Q*H*P*esize, Q*G*N*esize)";
         case SSD_ERR_MISALIGNED: return "a tensor pointer is not 16-byte aligned";
         case SSD_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than ssd_workspace_size()";
         case SSD_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
@@ -107,6 +111,13 @@ ssd_status ssd_check_dims(const ssd_dims* d) {
         return SSD_ERR_UNSUPPORTED;
     // grid limits: nchunks and nheads go in grid.x / grid.y, batch in grid.z
     if (nchunks_of(d) > INT32_MAX || d->nheads > 65535 || d->batch > 65535) return SSD_ERR_UNSUPPORTED;
+    // the kernels address one chunk's token rows of x, y, z, B and C with
+    // 32-bit offsets from the chunk's first row (buffer loads reach at most
+    // 2^31 - 1 bytes): a chunk's span of those rows must stay below 2^31 bytes
+    const int64_t esz = d->dtype == SSD_BF16 ? 2 : 4;
+    const int64_t span_x = d->chunk_size * d->nheads * d->headdim * esz;
+    const int64_t span_b = d->chunk_size * d->ngroups * d->dstate * esz;
+    if (span_x >= ((int64_t)1 << 31) || span_b >= ((int64_t)1 << 31)) return SSD_ERR_UNSUPPORTED;
     return SSD_OK;
 }
 

@@ -275,3 +275,83 @@ def test_gated_rmsnorm_argument_errors(lib):
     assert f(P(d), a, _fake(0x700004), a, ctypes.c_float(1e-5), 1, a, None) == MISAL
     assert f(P(dims(dtype=7)), a, None, a, ctypes.c_float(1e-5), 1, a, None) == UNSUP
     assert f(P(dims(seqlen=0)), None, None, None, ctypes.c_float(1e-5), 1, None, None) == OK
+
+
+# ---- the binding's argument checks (CPU tensors: rejected before any call) ----
+
+def _inputs(dtype=None, **over):
+    import torch
+    xt = dtype or torch.bfloat16
+    b, T, H, P, N, G = 2, 64, 4, 16, 16, 2
+    t = {"x": torch.zeros(b, T, H, P, dtype=xt), "dt": torch.zeros(b, T, H), "A": torch.zeros(H),
+         "B": torch.zeros(b, T, G, N, dtype=xt), "C": torch.zeros(b, T, G, N, dtype=xt), "D": torch.zeros(H)}
+    t.update(over)
+    return t
+
+
+@pytest.mark.parametrize("over,exc,what", [
+    (dict(dt="bf16"), TypeError, "dt must be torch.float32"),
+    (dict(A="short"), ValueError, "A must have shape"),
+    (dict(D="f64"), TypeError, "D must be torch.float32"),
+    (dict(C="f32"), TypeError, "C must be torch.bfloat16"),
+    (dict(C="short"), ValueError, "C must have shape"),
+    (dict(dt="short"), ValueError, "dt must have shape"),
+    (dict(), ValueError, "must be on a CUDA device"),
+])
+def test_binding_rejects_bad_tensors(lib, over, exc, what):
+    import torch
+    t = _inputs()
+    for k, v in over.items():
+        if v == "bf16":
+            t[k] = t[k].to(torch.bfloat16)
+        elif v == "f32":
+            t[k] = t[k].float()
+        elif v == "f64":
+            t[k] = t[k].double()
+        elif v == "short":
+            t[k] = t[k][..., :-1].contiguous() if t[k].dim() > 1 else t[k][:-1].contiguous()
+    with pytest.raises(exc, match=what):
+        ssd.forward(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], 32)
+
+
+def test_binding_rejects_bad_b_and_optional_tensors(lib):
+    import torch
+    t = _inputs()
+    with pytest.raises(TypeError, match="B must have x's type"):
+        ssd.forward(t["x"], t["dt"], t["A"], t["B"].float(), t["C"], t["D"], 32)
+    with pytest.raises(ValueError, match="B must be"):
+        ssd.forward(t["x"], t["dt"], t["A"], t["B"][:1].contiguous(), t["C"], t["D"], 32)
+    with pytest.raises(ValueError, match="initial_state must have shape"):
+        ssd.forward(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], 32,
+                    initial_state=torch.zeros(2, 4, 16, 15))
+    with pytest.raises(TypeError, match="seq_idx must be torch.int32"):
+        ssd.forward(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], 32,
+                    seq_idx=torch.zeros(2, 64, dtype=torch.int64))
+    with pytest.raises(TypeError, match="z must be torch.bfloat16"):
+        ssd.forward(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], 32, z=torch.zeros(2, 64, 4, 16))
+    d = ssd.dims_of(t["x"], t["B"], 32, "fp32")
+    with pytest.raises(TypeError, match="states must be torch.float32"):
+        ssd.ssd_state_passing(d, torch.zeros(2, 4, 2, 32), torch.zeros(2, 2, 4, 16, 16, dtype=torch.bfloat16),
+                              torch.zeros(2, 4, 16, 16))
+    with pytest.raises(ValueError, match="cs must have shape"):
+        ssd.ssd_chunk_cumsum(d, t["dt"], t["A"], torch.zeros(2, 4, 2, 31))
+    with pytest.raises(ValueError, match="state must have shape"):
+        ssd.step(t["x"][:, 0].contiguous(), t["dt"][:, 0].contiguous(), t["A"], t["B"][:, 0].contiguous(),
+                 t["C"][:, 0].contiguous(), t["D"], torch.zeros(2, 4, 16, 17))
+    with pytest.raises(ValueError, match="weight must be"):
+        ssd.gated_rmsnorm(t["x"], None, torch.zeros(3))
+
+
+def test_check_dims_rejects_chunk_spans_past_31_bits(lib):
+    # one chunk's rows of x span Q*H*P*esize bytes, addressed with 32-bit offsets
+    assert ssd.ssd_check_dims(dims(nheads=32767, ngroups=1, headdim=128, dstate=128)) == OK
+    assert ssd.ssd_check_dims(dims(nheads=32768, ngroups=1, headdim=128, dstate=128)) == UNSUP
+    assert ssd.ssd_check_dims(dims(dtype="fp32", nheads=32767, ngroups=1, headdim=128, dstate=64,
+                                   chunk_size=128)) == OK
+    assert ssd.ssd_check_dims(dims(dtype="fp32", nheads=32768, ngroups=1, headdim=128, dstate=64,
+                                   chunk_size=128)) == UNSUP
+    # B and C rows: Q*G*N*esize
+    assert ssd.ssd_check_dims(dims(dtype="fp32", nheads=8192, ngroups=8192, headdim=16, dstate=256,
+                                   chunk_size=256)) == UNSUP
+    assert ssd.ssd_check_dims(dims(dtype="fp32", nheads=8191, ngroups=8191, headdim=16, dstate=256,
+                                   chunk_size=256)) == OK
