@@ -3,15 +3,12 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload m2p7]
                     [--state-dtype fp32|bf16] [--no-cpu-baseline]
 
-One step is one ssd_forward call (a small launch that clears the look-back
-flags, the chunk-state kernel with the in-chunk prefix sums and the state
-passing folded in, then the chunk scan) over one batch of seeded synthetic
-input already resident in HBM; its wall clock gives tokens/s. Each kernel's
-average duration is measured in a second timed loop that makes the same
-launches through the stage entry points with HIP events between them on the
-launch stream; the single-stage kernels (chunk state alone, state passing
-alone, prefix sums alone) are timed the same way for their own rates. Rank 0
-prints one JSON line.
+One step is one ssd_forward call (three launches: the chunk-state kernel
+with the in-chunk prefix sums formed inside it, state passing, chunk scan)
+over one batch of seeded synthetic input already resident in HBM; its wall
+clock gives tokens/s. Each kernel's average duration is measured in a second
+timed loop that makes the same launches through the stage entry points with
+HIP events between them on the launch stream. Rank 0 prints one JSON line.
 
 Beside the headline figures the line carries: per-call medians of the
 forward with warm caches and with a 512 MB scrub written between calls (cold
@@ -39,16 +36,11 @@ METRIC = "SSD fwd tokens/sec at 2.7B-layer shape (L=4096, N=128); % MFMA/HBM roo
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFS = 2500.0  # dense bf16, TFLOP/s
 MFMA_F32_PEAK_TFS = 157.3
-# the launches of ssd_forward, by stage entry point: ssd_chunk_state_passing
-# (a clearing launch of the look-back flags, then the chunk-state kernel with
-# the prefix sums and the state passing folded in) and ssd_chunk_scan
-KERNELS = ["ssd_chunk_state_passing", "ssd_chunk_scan"]
-# single-stage kernels, timed on their own: ssd_chunk_cumsum_state (the chunk
-# state with the prefix sums formed inside) and ssd_state_passing
-STAGES = ["ssd_chunk_state", "ssd_state_passing"]
+# the launches of ssd_forward: ssd_chunk_cumsum_state runs the chunk-state
+# kernel with the in-chunk prefix sums formed inside it
+KERNELS = ["ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan"]
 SOURCES = {"ssd_chunk_cumsum": "chunk_cumsum.hip", "ssd_chunk_state": "chunk_state.hip",
-           "ssd_chunk_state_passing": "chunk_state.hip",
-           "ssd_state_passing": "state_passing.hip", "ssd_chunk_scan": "chunk_scan_impl.hpp"}
+           "ssd_state_passing": "state_passing.hip", "ssd_chunk_scan": "chunk_scan.hip"}
 
 
 def kernel_work(w, state_bytes: int) -> dict:
@@ -62,18 +54,7 @@ def kernel_work(w, state_bytes: int) -> dict:
     st = b * nc * H * N * P * state_bytes           # one pass over the chunk states
     st_in = b * (nc - 1) * H * N * P * state_bytes  # carried states read (h_0 = 0 is known)
     Qc = T / nc                                      # mean chunk length
-    # the chain of the look-back launch: each published state (all but the
-    # last chunk's, which is the final state) is read back by the next chunk's
-    # workgroup, with its bf16 residual when the storage is bf16
-    lo = b * (nc - 1) * H * N * P * 2 if state_bytes == 2 else 0
     return {
-        # reads x, B, dt; writes cs, the carried states h_1 .. h_{nc-1} and the
-        # final state. "chain_bytes": the residuals written and the chain's
-        # read-back of what it publishes (on top of the algorithmic bytes)
-        "ssd_chunk_state_passing": {"bytes": e * b * T * (H * P + G * N) + 4 * b * T * H + 4 * b * H * nc * Q + st_in
-                                    + 4 * b * H * N * P,
-                                    "flops": 2 * b * T * H * N * P + b * T * H + 2 * b * nc * H * N * P,
-                                    "chain_bytes": lo + st_in + lo},
         "ssd_chunk_cumsum": {"bytes": 4 * b * T * H + 4 * b * H * nc * Q, "flops": b * T * H},
         # with the prefix sums formed inside: reads x, B, dt; writes cs and the states
         "ssd_chunk_state": {"bytes": e * b * T * (H * P + G * N) + 4 * b * T * H + 4 * b * H * nc * Q + st,
@@ -383,8 +364,6 @@ def main() -> int:
     final = torch.empty((w.batch, w.nheads, w.dstate, w.headdim), dtype=torch.float32, device=dev)
     y = torch.empty_like(g["x"])
     ws = ssd.alloc_workspace(d, dev)
-    nscr = ssd.ssd_lookback_scratch_size(d)
-    scratch = torch.empty(nscr, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     sh = stream.cuda_stream
 
@@ -393,24 +372,15 @@ def main() -> int:
         # HIP events between them on the launch stream
         if ev is not None:
             ev[0].record(stream)
-        ssd.ssd_chunk_state_passing(d, g["x"], g["dt"], g["A"], g["B"], None, cs, states, final, scratch, nscr, sh)
-        if ev is not None:
-            ev[1].record(stream)
-        ssd.ssd_chunk_scan(d, g["x"], g["dt"], g["B"], g["C"], g["D"], cs, states, y, sh)
-        if ev is not None:
-            ev[2].record(stream)
-
-    def single_stages(ev=None):
-        # the chunk state (prefix sums formed inside) and the state passing as
-        # single stages, for their own rates
-        if ev is not None:
-            ev[0].record(stream)
         ssd.ssd_chunk_cumsum_state(d, g["x"], g["dt"], g["A"], g["B"], cs, states, sh)
         if ev is not None:
             ev[1].record(stream)
         ssd.ssd_state_passing(d, cs, states, final, sh)
         if ev is not None:
             ev[2].record(stream)
+        ssd.ssd_chunk_scan(d, g["x"], g["dt"], g["B"], g["C"], g["D"], cs, states, y, sh)
+        if ev is not None:
+            ev[3].record(stream)
 
     def forward():
         ssd.ssd_forward(d, g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], y, final, ws, ws.numel(), sh)
@@ -469,19 +439,6 @@ def main() -> int:
     staged_ms = (time.perf_counter() - t1) * 1e3 / args.steps
     kms = {name: sum(events[k][i].elapsed_time(events[k][i + 1]) for k in range(args.steps)) / args.steps
            for i, name in enumerate(KERNELS)}
-    lb_status = ssd.ssd_lookback_status(scratch, sh)
-    if lb_status != 0:
-        raise RuntimeError(f"look-back wait gave up (status {lb_status})")
-
-    for _ in range(args.warmup):
-        single_stages()
-    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STAGES) + 1)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for k in range(args.steps):
-        single_stages(sev[k])
-    torch.cuda.synchronize()
-    sms = {name: sum(sev[k][i].elapsed_time(sev[k][i + 1]) for k in range(args.steps)) / args.steps
-           for i, name in enumerate(STAGES)}
 
     # the in-chunk prefix sums alone (ssd_chunk_cumsum, the stage that the
     # forward forms inside the chunk-state launch), for its own HBM rate
@@ -643,20 +600,9 @@ def main() -> int:
                             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
                             "TFLOP/s": round(tfs, 2), "mfma_frac": round(tfs / peak_tf, 4),
                             "alg_bytes": work[name]["bytes"], "alg_flops": work[name]["flops"]}
-    ch = work["ssd_chunk_state_passing"]
-    t = kms["ssd_chunk_state_passing"] * 1e-3
-    per_kernel["ssd_chunk_state_passing"]["chain_bytes"] = ch["chain_bytes"]
-    per_kernel["ssd_chunk_state_passing"]["GB/s_with_chain"] = round((ch["bytes"] + ch["chain_bytes"]) / t / 1e9, 1)
-    for name in STAGES:
-        t = sms[name] * 1e-3
-        gbs = work[name]["bytes"] / t / 1e9
-        per_kernel[f"{name} (single stage)"] = {
-            "ms": round(sms[name], 5), "GB/s": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-            "alg_bytes": work[name]["bytes"],
-            "note": "not launched by ssd_forward (folded into ssd_chunk_state_passing); timed alone"}
     cw = kernel_work(w, sbytes)["ssd_chunk_cumsum"]
     cum_gbs = cw["bytes"] / (cum_ms * 1e-3) / 1e9
-    per_kernel["ssd_chunk_cumsum (single stage)"] = {
+    per_kernel["ssd_chunk_cumsum (standalone stage)"] = {
         "ms": round(cum_ms, 5), "GB/s": round(cum_gbs, 1), "hbm_frac": round(cum_gbs / HBM_PEAK_GBS, 4),
         "alg_bytes": cw["bytes"], "note": "formed inside the chunk-state launch in ssd_forward; timed alone here"}
     dom = max(KERNELS, key=lambda n: kms[n])

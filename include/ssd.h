@@ -14,7 +14,7 @@
  *
  * Entry points: ssd_forward (the whole transform) and its stages
  * (ssd_chunk_cumsum, ssd_chunk_state, ssd_chunk_cumsum_state,
- * ssd_chunk_state_passing, ssd_state_passing, ssd_chunk_scan); from a given initial state
+ * ssd_state_passing, ssd_chunk_scan); from a given initial state
  * (ssd_forward_init, ssd_state_passing_init, ssd_chunk_scan_init); with the
  * block's output gate (ssd_forward_gated) and the norm after it
  * (ssd_gated_rmsnorm); over rows packing several documents
@@ -97,28 +97,9 @@ const char* ssd_status_string(ssd_status s);
 ssd_status ssd_check_dims(const ssd_dims* d);
 
 /* Bytes of device workspace ssd_forward needs for `d`; 0 when `d` is invalid
- * (and for batch == 0 or seqlen == 0, which need none). The workspace holds,
- * in this order and each at a 256-byte aligned offset, the look-back scratch
- * (ssd_lookback_scratch_size), the cs buffer and the states buffer below. */
+ * (and for batch == 0 or seqlen == 0, which need none). The workspace holds
+ * the cs buffer and the states buffer below, each at a 256-byte aligned offset. */
 size_t ssd_workspace_size(const ssd_dims* d);
-
-/* Bytes of the scratch of ssd_chunk_state_passing for `d` (0 when `d` is
- * invalid or empty): a 32-bit ticket counter, a status word and one flag per
- * (batch, chunk, head), rounded up to 256 bytes; with bf16 state storage also
- * the bf16 residual of every published state, [b, nc, H, P, N]. ssd_forward
- * keeps it at the start of its workspace. */
-size_t ssd_lookback_scratch_size(const ssd_dims* d);
-
-/* Status of the look-back waits of the last ssd_chunk_state_passing (or
- * ssd_forward*) call that used `scratch` (for ssd_forward*: the workspace):
- * synchronises `stream`, then reads the status word into *status: 0 when every
- * wait ended normally, bit 0 set when some wait gave up after its poll limit
- * (the results of that call are then invalid). The poll limit is 2^20 polls,
- * or the value of the environment variable SSD_LOOKBACK_SPIN when set (read at
- * every call; negative: every wait gives up at once, for tests of this path).
- * Errors: SSD_ERR_NULL_POINTER, SSD_ERR_MISALIGNED, SSD_ERR_LAUNCH (the HIP
- * runtime failed to synchronise or copy). Blocks the calling thread. */
-ssd_status ssd_lookback_status(const void* scratch, int32_t* status, hipStream_t stream);
 
 /* Bytes of the two stage buffers for the stage entry points: cs [b,H,nc,Q] fp32
  * and states [b,nc,H,P,N] in d->state_dtype. Either output pointer may be NULL.
@@ -129,13 +110,9 @@ ssd_status ssd_stage_sizes(const ssd_dims* d, size_t* cs_bytes, size_t* states_b
  * Full forward: Knowl 2's inputs X, A, B, C and chunk size Q, its outputs Y and
  * h_final (the algorithm's inputs and outputs), with the per-head
  * discretisation dt, A and the skip term D. Enqueues, in order,
- * ssd_chunk_state_passing (stages 1, 2 and 3: a small clearing launch, then
- * one launch) and ssd_chunk_scan (stage 4), with cs, states and the look-back
- * scratch in the workspace; the result is bitwise that of those two stage
- * entry points run one after the other. With fp32 state storage it is also
- * bitwise that of the four single-stage entry points; with bf16 storage the
- * chain of carried states runs at higher precision than ssd_state_passing's
- * (see ssd_chunk_state_passing).
+ * ssd_chunk_cumsum_state (stages 1 and 2 in one launch), ssd_state_passing
+ * and ssd_chunk_scan; the result is bitwise that of the four stage entry
+ * points run one after another.
  *   x [b,T,H,P], dt [b,T,H], A [H], B [b,T,G,N], C [b,T,G,N], D [H]: inputs
  *   y [b,T,H,P] (out, dtype), final_state [b,H,N,P] (out, fp32)
  *   workspace: device buffer of at least ssd_workspace_size(d) bytes; its
@@ -151,8 +128,8 @@ ssd_status ssd_forward(const ssd_dims* d, const void* x, const float* dt, const 
  * at h_{-1} = initial_state instead of zero (so that a sequence can be resumed
  * from the final state of its prefix). initial_state [b,H,N,P] fp32 (device,
  * caller-owned, read only; 16-byte aligned), or NULL for a zero state, which
- * gives exactly ssd_forward. Enqueues ssd_chunk_state_passing (from the
- * initial state) and ssd_chunk_scan_init. With T = 0, final_state
+ * gives exactly ssd_forward. Enqueues ssd_chunk_cumsum_state,
+ * ssd_state_passing_init and ssd_chunk_scan_init. With T = 0, final_state
  * receives a copy of initial_state. Other arguments and errors as ssd_forward.
  */
 ssd_status ssd_forward_init(const ssd_dims* d, const void* x, const float* dt, const float* A,
@@ -301,32 +278,6 @@ ssd_status ssd_chunk_state(const ssd_dims* d, const void* x, const float* dt, co
  */
 ssd_status ssd_chunk_cumsum_state(const ssd_dims* d, const void* x, const float* dt, const float* A,
                                   const void* B, float* cs, void* states, hipStream_t stream);
-
-/*
- * Stages 1, 2 and 3 in one launch (Knowl 2: the in-chunk prefix sums, the
- * chunk states, and the loop h_{c+1} = (prod a) h_c + S_c over chunks), what
- * ssd_forward runs. Workgroups take their (chunk, heads) in the order of an
- * atomic ticket, chunk-major; the workgroup of chunk c forms S_c, waits (with a
- * bounded poll, see ssd_lookback_status) until that of chunk c - 1 has
- * published h_c, and publishes h_{c+1}, so S_c never goes to memory.
- *   x, dt, A, B in; initial_state [b,H,N,P] fp32 or NULL (zero);
- *   cs [b,H,nc,Q] out (as ssd_chunk_cumsum);
- *   states [b,nc,H,P,N] out: states[c] = h_c, the state entering chunk c, for
- *     c >= 1 (as ssd_state_passing writes it); states[0] is written (h_0) only
- *     with an initial state;
- *   final_state [b,H,N,P] fp32 out;
- *   scratch: at least ssd_lookback_scratch_size(d) bytes, contents on entry do
- *     not matter (a clearing launch precedes the main one). With bf16 storage
- *     it also receives h - bf16(h) of every published state, and the chain
- *     reads h back as bf16(h) + that residual: about 16 significant bits per
- *     link, so rounding does not compound along long sequences; the states
- *     buffer keeps bf16(h) for the chunk scan.
- * Calls that share a scratch buffer must not overlap in time. Errors as
- * ssd_forward_init, with SSD_ERR_WORKSPACE_TOO_SMALL for a short scratch.
- */
-ssd_status ssd_chunk_state_passing(const ssd_dims* d, const void* x, const float* dt, const float* A, const void* B,
-                                   const float* initial_state, float* cs, void* states, float* final_state,
-                                   void* scratch, size_t scratch_bytes, hipStream_t stream);
 
 /*
  * Stage 3 (Knowl 2, the sequential loop over chunks h_{c+1} = (prod a) h_c + S_c,

@@ -86,11 +86,6 @@ def load_library() -> ctypes.CDLL:
     lib.ssd_chunk_scan_init.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.ssd_chunk_scan_init.restype = st
     lib.ssd_step.argtypes, lib.ssd_step.restype = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp], st
-    lib.ssd_lookback_scratch_size.argtypes, lib.ssd_lookback_scratch_size.restype = [P], sz
-    lib.ssd_lookback_status.argtypes = [vp, ctypes.POINTER(ctypes.c_int32), vp]
-    lib.ssd_lookback_status.restype = st
-    lib.ssd_chunk_state_passing.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-    lib.ssd_chunk_state_passing.restype = st
     _lib = lib
     return lib
 
@@ -247,19 +242,6 @@ def ssd_workspace_size(d: SsdDims) -> int:
     return load_library().ssd_workspace_size(ctypes.byref(d))
 
 
-def ssd_lookback_scratch_size(d: SsdDims) -> int:
-    return load_library().ssd_lookback_scratch_size(ctypes.byref(d))
-
-
-def ssd_lookback_status(scratch, stream=None) -> int:
-    """Synchronise the stream and return the look-back status word of the last
-    call that used `scratch` (or a forward's workspace): 0 = every wait ended."""
-    s = _stream(scratch.device) if stream is None else stream
-    v = ctypes.c_int32(-1)
-    _check(load_library().ssd_lookback_status(_ptr(scratch), ctypes.byref(v), s))
-    return v.value
-
-
 def ssd_stage_sizes(d: SsdDims) -> tuple[int, int]:
     cs, st = ctypes.c_size_t(0), ctypes.c_size_t(0)
     _check(load_library().ssd_stage_sizes(ctypes.byref(d), ctypes.byref(cs), ctypes.byref(st)))
@@ -367,16 +349,6 @@ def ssd_chunk_cumsum_state(d, x, dt, A, B, cs, states, stream=None):
     s = _stream(x.device) if stream is None else stream
     _check(load_library().ssd_chunk_cumsum_state(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
                                                  _ptr(cs), _ptr(states), s))
-
-
-def ssd_chunk_state_passing(d, x, dt, A, B, initial_state, cs, states, final_state, scratch, scratch_bytes,
-                            stream=None):
-    _check_io(d, x=x, dt=dt, A=A, B=B, initial_state=initial_state, cs=cs, states=states, final_state=final_state)
-    _check_workspace(scratch, scratch_bytes, _device_of(x))
-    s = _stream(x.device) if stream is None else stream
-    _check(load_library().ssd_chunk_state_passing(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
-                                                  _ptr(initial_state), _ptr(cs), _ptr(states), _ptr(final_state),
-                                                  _ptr(scratch), scratch_bytes, s))
 
 
 def ssd_state_passing(d, cs, states, final_state, stream=None):

@@ -92,144 +92,17 @@ __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t rs, uint32_t voff, u
 
 constexpr uint32_t kOob = 0x80000000u;   // buffer offset past every range: the copy reads 0
 
-// The look-back link of chunk c for this workgroup's heads (see LB below):
-// wait until the workgroup of chunk c - 1 has published h_c, then
-//   h_{c+1} = exp(lam) h_c + S_c   (h_0: the initial state, or zero)
-// with S_c in the accumulators, and publish h_{c+1}: into states[c + 1]
-// (the chunk scan's carried state; bf16 storage also keeps the residual
-// h - bf16(h) in states_lo, so that the chain itself runs at about 16
-// significant bits per link and rounding does not compound along it), or
-// into the final state [N][P] after the last chunk. With an initial state,
-// states[0] receives it (rounded to the storage type). Then this
-// workgroup's flag is set. Lane (l32, hf) works on state row
-// p = (pt0 + i) 32 + l32 and, after swapping accumulator quarters with its
-// partner lane (v_permlane32_swap), on 8 consecutive columns n of it.
-template <typename ST, int PTW, int NT>
-__device__ __forceinline__ void lookback_link(const Params& p, f32x16 (&acc)[PTW][NT], const float* lb_lam, int64_t b,
-                                              int c, int64_t h0, int hh, int pt0, bool active, int lane) {
-    const int64_t H = p.nheads, P = p.headdim, N = p.dstate, nc = p.nchunks;
-    const int hf = lane >> 5, l32 = lane & 31;
-    const int64_t flag_self = ((int64_t)b * nc + c) * H + h0;
-    if (c > 0) {
-        if (threadIdx.x == 0) {
-            const int* fl = p.lb_flags + (flag_self - H);   // chunk c - 1, same heads
-            bool ok = p.lb_spin >= 0;
-            for (int n = 0; ok && __hip_atomic_load(fl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0; ++n) {
-                if (n >= p.lb_spin) ok = false;
-                else __builtin_amdgcn_s_sleep(4);
-            }
-            if (!ok) atomicOr(p.lb_status, 1);
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        }
-        __syncthreads();
-    }
-    if (active) {
-        const int64_t h = h0 + hh;
-        const float a = exp2f(lb_lam[hh] * kLog2e);
-        ST* const sbase = static_cast<ST*>(p.states);
-        bf16* const lbase = static_cast<bf16*>(p.states_lo);
-        const int64_t in_off = (((int64_t)b * nc + c) * H + h) * P * N;     // h_c
-        const int64_t out_off = in_off + H * P * N;                          // h_{c+1}
-        const float* ini = p.init_state ? p.init_state + (b * H + h) * N * P : nullptr;
-        float* fin = p.final_state + (b * H + h) * N * P;
-        const bool last_chunk = c == nc - 1;
-#pragma unroll
-        for (int i = 0; i < PTW; ++i) {
-            const int pr = (pt0 + i) * 32 + l32;
-#pragma unroll
-            for (int n = 0; n < NT; ++n) {
-#pragma unroll
-                for (int gp = 0; gp < 2; ++gp) {
-                    float s8[8];
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[i][n][8 * gp + r]),
-                                                                         __float_as_uint(acc[i][n][8 * gp + 4 + r]),
-                                                                         false, false);
-                        s8[r] = __uint_as_float(sw[0]);
-                        s8[4 + r] = __uint_as_float(sw[1]);
-                    }
-                    const int col = n * 32 + 8 * (2 * gp + hf);
-                    if (pr >= P || col >= N) continue;
-                    const int64_t e = (int64_t)pr * N + col;
-                    float hp[8];
-                    if (c > 0) {
-                        if constexpr (sizeof(ST) == 2) {
-                            const bf16x8 hi = ldg8(sbase + in_off + e);
-                            const bf16x8 lo = ldg8(lbase + in_off + e);
-#pragma unroll
-                            for (int k = 0; k < 8; ++k) hp[k] = to_f32(hi[k]) + to_f32(lo[k]);
-                        } else {
-                            const f32x8 v = ldg8(reinterpret_cast<const float*>(sbase) + in_off + e);
-#pragma unroll
-                            for (int k = 0; k < 8; ++k) hp[k] = v[k];
-                        }
-                    } else if (ini) {
-#pragma unroll
-                        for (int k = 0; k < 8; ++k) hp[k] = ldg(ini + (int64_t)(col + k) * P + pr);
-                        typename Vec8<ST>::type o;
-#pragma unroll
-                        for (int k = 0; k < 8; ++k) o[k] = from_f32<ST>(hp[k]);
-                        store8(sbase + in_off + e, o);
-                    } else {
-#pragma unroll
-                        for (int k = 0; k < 8; ++k) hp[k] = 0.0f;
-                    }
-                    float hn[8];
-#pragma unroll
-                    for (int k = 0; k < 8; ++k) hn[k] = a * hp[k] + s8[k];
-                    if (last_chunk) {
-#pragma unroll
-                        for (int k = 0; k < 8; ++k) stg(fin + (int64_t)(col + k) * P + pr, hn[k]);
-                    } else if constexpr (sizeof(ST) == 2) {
-                        bf16x8 hi, lo;
-#pragma unroll
-                        for (int k = 0; k < 8; ++k) {
-                            hi[k] = from_f32<bf16>(hn[k]);
-                            lo[k] = from_f32<bf16>(hn[k] - to_f32(hi[k]));
-                        }
-                        stg(reinterpret_cast<bf16x8*>(sbase + out_off + e), hi);
-                        stg(reinterpret_cast<bf16x8*>(lbase + out_off + e), lo);
-                    } else {
-                        f32x8 o;
-#pragma unroll
-                        for (int k = 0; k < 8; ++k) o[k] = hn[k];
-                        store8(reinterpret_cast<float*>(sbase) + out_off + e, o);
-                    }
-                }
-            }
-        }
-    }
-    // every store of the workgroup completes, then one release at device
-    // scope and the flag
-    wait_vmem();
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        __hip_atomic_store(p.lb_flags + flag_self, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-}
-
 // FUSED: also compute (and write) cs from dt and A, the step of
 // ssd_chunk_cumsum; else read the given cs. VARLEN (with FUSED only): packed
 // documents, w_j = 0 for tokens outside the document of the chunk's last
 // token (the decay is 0 at a document start, "Transformers are SSMs", Knowl 8).
-// LB (with FUSED only): the state passing of Knowl 2 (h_{c+1} = exp(cs_last)
-// h_c + S_c) is done here as an ordered look-back: workgroups take chunks in
-// the order of an atomic ticket, chunk-major, so the workgroup of chunk c - 1
-// (same batch row and heads) has always started before that of chunk c. After
-// its own S_c, the workgroup of chunk c waits (bounded) for its predecessor's
-// flag, reads h_c, and publishes h_{c+1} (the final state after the last
-// chunk) and its own flag. S_c itself never leaves the chip.
-template <typename T, int PT, int NT, typename ST, bool FUSED, bool VARLEN, bool LB>
+template <typename T, int PT, int NT, typename ST, bool FUSED, bool VARLEN>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void ssd_chunk_state_kernel(Params p) {
     using Cfg = StateCfg<T, PT, NT>;
     using V8 = typename Vec8<T>::type;
     constexpr int HPW = Cfg::HPW, WPH = Cfg::WPH, PTW = Cfg::PTW;
     constexpr int ESZ = (int)sizeof(T);
     __shared__ __attribute__((aligned(1024))) unsigned char smem[Cfg::LDS];
-    __shared__ float lb_lam[HPW];   // LB: log of each head's decay over the chunk (-inf: no state passes)
-    __shared__ int lb_tk;           // LB: this workgroup's ticket
     constexpr int NBUF = Cfg::NBUF;
     float* wv = reinterpret_cast<float*>(smem + NBUF * Cfg::BUF);   // [HPW][Q]: dt, then w
 
@@ -237,30 +110,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int64_t T_ = p.seqlen, H = p.nheads, P = p.headdim, N = p.dstate, G = p.ngroups;
     const int64_t hpg = p.heads_per_group, nc = p.nchunks;
     const int nhb = (int)((hpg + HPW - 1) / HPW);
-    int hb_, c_;
-    int64_t g_, b_;
-    if constexpr (LB) {
-        // ticket order, chunk-major: (chunk, batch, group, head block)
-        if (threadIdx.x == 0) lb_tk = (int)atomicAdd(p.lb_counter, 1u);
-        __syncthreads();
-        const int t = lb_tk, per_chunk = (int)(p.batch * G) * nhb;
-        c_ = t / per_chunk;
-        const int r = t - c_ * per_chunk;
-        b_ = r / (int)(G * nhb);
-        const int r2 = r - (int)b_ * (int)(G * nhb);
-        g_ = r2 / nhb;
-        hb_ = r2 - (int)g_ * nhb;
-    } else {
-        const int lin = xcd_logical_block();
-        int bx = lin % (int)gridDim.x;
-        hb_ = bx % nhb;
-        bx /= nhb;
-        g_ = bx % G;
-        c_ = (int)(bx / G);
-        b_ = lin / (int)gridDim.x;
-    }
-    const int hb = hb_, c = c_;
-    const int64_t g = g_, b = b_;
+    const int lin = xcd_logical_block();
+    int bx = lin % (int)gridDim.x;
+    const int hb = bx % nhb;
+    bx /= nhb;
+    const int64_t g = bx % G;
+    const int c = (int)(bx / G);
+    const int64_t b = lin / (int)gridDim.x;
     const int64_t h0 = g * hpg + (int64_t)hb * HPW;
     const int nh = (int)min<int64_t>(HPW, hpg - (int64_t)hb * HPW);
     const int64_t t0 = (int64_t)c * Q;
@@ -382,14 +238,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         int slast = 0;
         const int* sq = VARLEN ? p.seq_idx + b * T_ + t0 : nullptr;
         if constexpr (VARLEN) slast = sq[qc - 1];
-        if constexpr (LB) {
-            // the chunk's decay; a chunk in which a document starts (its last
-            // token's id differs from the token before it, or from the row's
-            // first token for chunk 0) passes no state on (decay exactly 0)
-            float lam = last;
-            if constexpr (VARLEN) lam = slast == (c > 0 ? sq[-1] : sq[0]) ? last : -INFINITY;
-            if (lane == 0 && hq < nh) lb_lam[hq] = lam;
-        }
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int j = lane * per + k;
@@ -468,9 +316,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             for (int k = 0; k < per; ++k) out[k] = csv[k];
         }
     }
-    if constexpr (LB) {
-        lookback_link<ST, PTW, NT>(p, acc, lb_lam, b, c, h0, hh, pt0, active, lane);
-    } else if (active) {
+    if (active) {
         // accumulator element r of tile (i, n): state row p = (pt0+i)*32 + l32,
         // column n*32 + 8*(r/4) + 4*hf + r%4. bf16: the lane halves swap the
         // halves of quarters 2g and 2g+1 (v_permlane32_swap), so that a lane
@@ -532,19 +378,12 @@ static hipError_t launch_cs(const Params& p, hipStream_t s) {
     using Cfg = StateCfg<T, PT, NT>;
     const int64_t nhb = (p.heads_per_group + Cfg::HPW - 1) / Cfg::HPW;
     dim3 grid((unsigned)(p.nchunks * p.ngroups * nhb), (unsigned)p.batch);
-    if (p.lb_counter) {
-        // look-back: a 1-D grid; the ticket, not the block index, picks the work
-        dim3 g1((unsigned)(p.nchunks * p.ngroups * nhb * p.batch));
-        if (p.seq_idx)
-            hipLaunchKernelGGL((ssd_chunk_state_kernel<T, PT, NT, ST, true, true, true>), g1, dim3(256), 0, s, p);
-        else
-            hipLaunchKernelGGL((ssd_chunk_state_kernel<T, PT, NT, ST, true, false, true>), g1, dim3(256), 0, s, p);
-    } else if (p.fuse_cs && p.seq_idx)
-        hipLaunchKernelGGL((ssd_chunk_state_kernel<T, PT, NT, ST, true, true, false>), grid, dim3(256), 0, s, p);
+    if (p.fuse_cs && p.seq_idx)
+        hipLaunchKernelGGL((ssd_chunk_state_kernel<T, PT, NT, ST, true, true>), grid, dim3(256), 0, s, p);
     else if (p.fuse_cs)
-        hipLaunchKernelGGL((ssd_chunk_state_kernel<T, PT, NT, ST, true, false, false>), grid, dim3(256), 0, s, p);
+        hipLaunchKernelGGL((ssd_chunk_state_kernel<T, PT, NT, ST, true, false>), grid, dim3(256), 0, s, p);
     else if (!p.seq_idx)
-        hipLaunchKernelGGL((ssd_chunk_state_kernel<T, PT, NT, ST, false, false, false>), grid, dim3(256), 0, s, p);
+        hipLaunchKernelGGL((ssd_chunk_state_kernel<T, PT, NT, ST, false, false>), grid, dim3(256), 0, s, p);
     else
         return hipErrorInvalidValue;   // document resets need the fused prefix sums
     return hipGetLastError();

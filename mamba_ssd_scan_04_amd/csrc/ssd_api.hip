@@ -1,7 +1,6 @@
 // The C ABI of libssd (declared in include/ssd.h): argument checks, workspace
 // layout and the launch order of the four kernels. No allocation, no state.
 #include <stdint.h>
-#include <stdlib.h>
 
 #include <atomic>
 
@@ -69,26 +68,6 @@ ssd::Params make_params(const ssd_dims* d) {
 
 ssd_status to_status(hipError_t e) { return e == hipSuccess ? SSD_OK : SSD_ERR_LAUNCH; }
 
-// The look-back scratch of the chunk-state launch that passes the states on:
-// [counter, status, flags [b, nc, H]] as 32-bit words, then (bf16 storage)
-// the residual states [b, nc, H, P, N] bf16.
-size_t lb_header_bytes(const ssd_dims* d) {
-    return round_up((size_t)(2 + d->batch * nchunks_of(d) * d->nheads) * sizeof(int32_t));
-}
-size_t lb_scratch_bytes(const ssd_dims* d) {
-    return lb_header_bytes(d) + (d->state_dtype == SSD_BF16 ? round_up(states_bytes_of(d)) : 0);
-}
-
-// Polls of a look-back flag before the wait gives up: SSD_LOOKBACK_SPIN
-// (negative: give up at once, for tests of the error path), else 2^20
-// (seconds of waiting; a wait in a correct launch lasts microseconds).
-int lookback_spin() {
-    const char* v = getenv("SSD_LOOKBACK_SPIN");
-    if (!v || !*v) return 1 << 20;
-    const long n = strtol(v, nullptr, 10);
-    return n < 0 ? -1 : (int)(n > (1L << 30) ? (1L << 30) : n);
-}
-
 bool empty(const ssd_dims* d) { return d->batch == 0 || d->seqlen == 0; }
 
 }  // namespace
@@ -152,23 +131,7 @@ ssd_status ssd_stage_sizes(const ssd_dims* d, size_t* cs_bytes, size_t* states_b
 
 size_t ssd_workspace_size(const ssd_dims* d) {
     if (ssd_check_dims(d) != SSD_OK || empty(d)) return 0;
-    return lb_scratch_bytes(d) + round_up(cs_bytes_of(d)) + round_up(states_bytes_of(d));
-}
-
-size_t ssd_lookback_scratch_size(const ssd_dims* d) {
-    if (ssd_check_dims(d) != SSD_OK || empty(d)) return 0;
-    return lb_scratch_bytes(d);
-}
-
-ssd_status ssd_lookback_status(const void* scratch, int32_t* status, hipStream_t stream) {
-    if (!scratch || !status) return SSD_ERR_NULL_POINTER;
-    if (!aligned16(scratch)) return SSD_ERR_MISALIGNED;
-    if (hipStreamSynchronize(stream) != hipSuccess) return SSD_ERR_LAUNCH;
-    int32_t v = 0;
-    if (hipMemcpy(&v, static_cast<const int32_t*>(scratch) + 1, sizeof(v), hipMemcpyDeviceToHost) != hipSuccess)
-        return SSD_ERR_LAUNCH;
-    *status = v;
-    return SSD_OK;
+    return round_up(cs_bytes_of(d)) + round_up(states_bytes_of(d));
 }
 
 ssd_status ssd_chunk_cumsum(const ssd_dims* d, const float* dt, const float* A, float* cs,
@@ -274,47 +237,6 @@ ssd_status chunk_scan_impl(const ssd_dims* d, const void* x, const float* dt, co
     return to_status(ssd::launch_chunk_scan(p, d->dtype, d->state_dtype, stream));
 }
 
-// The chunk-state launch with the state passing folded in (ordered look-back):
-// the look-back header is cleared first, then one launch forms cs, the chunk
-// states and their chain, writing h_c into states[c] (c >= 1; states[0] only
-// with an initial state) and the final state.
-ssd_status chunk_state_passing_impl(const ssd_dims* d, const void* x, const float* dt, const float* A, const void* B,
-                                    const float* init, float* cs, void* states, float* final_state, void* scratch,
-                                    size_t scratch_bytes, hipStream_t stream, const int* seq = nullptr) {
-    ssd_status st = ssd_check_dims(d);
-    if (st != SSD_OK) return st;
-    if (d->batch == 0) return SSD_OK;
-    if (d->seqlen == 0) return state_passing_impl(d, nullptr, nullptr, init, final_state, stream);
-    if (!x || !dt || !A || !B || !cs || !states || !final_state || !scratch) return SSD_ERR_NULL_POINTER;
-    if (!aligned16(x) || !aligned16(dt) || !aligned16(A) || !aligned16(B) || !aligned16(cs) || !aligned16(states) ||
-        !aligned16(final_state) || !aligned16(scratch) || (init && !aligned16(init)))
-        return SSD_ERR_MISALIGNED;
-    if (scratch_bytes < lb_scratch_bytes(d)) return SSD_ERR_WORKSPACE_TOO_SMALL;
-    int32_t* hdr = static_cast<int32_t*>(scratch);
-    const int64_t nflags = d->batch * nchunks_of(d) * d->nheads;
-    // tickets and flag indices are 32-bit (there are at most nflags workgroups)
-    if (nflags > INT32_MAX - 2) return SSD_ERR_UNSUPPORTED;
-    hipError_t e = ssd::launch_zero_fill(reinterpret_cast<float*>(hdr), 2 + nflags, stream);
-    if (e != hipSuccess) return SSD_ERR_LAUNCH;
-    ssd::Params p = make_params(d);
-    p.x = x;
-    p.dt = dt;
-    p.A = A;
-    p.B = B;
-    p.cs = cs;
-    p.states = states;
-    p.fuse_cs = 1;
-    p.init_state = init;
-    p.final_state = final_state;
-    p.seq_idx = seq;
-    p.lb_counter = reinterpret_cast<unsigned int*>(hdr);
-    p.lb_status = hdr + 1;
-    p.lb_flags = hdr + 2;
-    p.states_lo = d->state_dtype == SSD_BF16 ? static_cast<unsigned char*>(scratch) + lb_header_bytes(d) : nullptr;
-    p.lb_spin = lookback_spin();
-    return to_status(ssd::launch_chunk_state(p, d->dtype, d->state_dtype, stream));
-}
-
 ssd_status forward_impl(const ssd_dims* d, const void* x, const float* dt, const float* A, const void* B,
                         const void* C, const float* D, const float* init, const void* z, void* y,
                         float* final_state, void* workspace, size_t workspace_bytes, hipStream_t stream,
@@ -330,12 +252,23 @@ ssd_status forward_impl(const ssd_dims* d, const void* x, const float* dt, const
         (z && !aligned16(z)))
         return SSD_ERR_MISALIGNED;
     if (workspace_bytes < ssd_workspace_size(d)) return SSD_ERR_WORKSPACE_TOO_SMALL;
-    // workspace: [look-back scratch][cs][states]
-    unsigned char* ws = static_cast<unsigned char*>(workspace);
-    const size_t lb = lb_scratch_bytes(d);
-    float* cs = reinterpret_cast<float*>(ws + lb);
-    void* states = ws + lb + round_up(cs_bytes_of(d));
-    st = chunk_state_passing_impl(d, x, dt, A, B, init, cs, states, final_state, ws, lb, stream, seq);
+    float* cs = static_cast<float*>(workspace);
+    void* states = static_cast<unsigned char*>(workspace) + round_up(cs_bytes_of(d));
+    if (seq) {   // the fused chunk-state launch, with the document masks
+        ssd::Params p = make_params(d);
+        p.x = x;
+        p.dt = dt;
+        p.A = A;
+        p.B = B;
+        p.cs = cs;
+        p.states = states;
+        p.fuse_cs = 1;
+        p.seq_idx = seq;
+        st = to_status(ssd::launch_chunk_state(p, d->dtype, d->state_dtype, stream));
+    } else {
+        st = ssd_chunk_cumsum_state(d, x, dt, A, B, cs, states, stream);
+    }
+    if (st == SSD_OK) st = state_passing_impl(d, cs, states, init, final_state, stream, seq);
     if (st == SSD_OK) st = chunk_scan_impl(d, x, dt, B, C, D, cs, states, init ? 1 : 0, z, y, stream, seq);
     return st;
 }
@@ -343,13 +276,6 @@ ssd_status forward_impl(const ssd_dims* d, const void* x, const float* dt, const
 }  // namespace
 
 extern "C" {
-
-ssd_status ssd_chunk_state_passing(const ssd_dims* d, const void* x, const float* dt, const float* A, const void* B,
-                                   const float* initial_state, float* cs, void* states, float* final_state,
-                                   void* scratch, size_t scratch_bytes, hipStream_t stream) {
-    return chunk_state_passing_impl(d, x, dt, A, B, initial_state, cs, states, final_state, scratch, scratch_bytes,
-                                    stream);
-}
 
 ssd_status ssd_state_passing(const ssd_dims* d, const float* cs, void* states, float* final_state,
                              hipStream_t stream) {

@@ -47,15 +47,6 @@ struct Params {
     const void* z;             // gate input [b,T,H,P] (x's type): y *= silu(z); nullptr: no gate
     const int* seq_idx;        // document ids [b,T], non-decreasing along T: the state is reset where
                                // the id changes; nullptr: one sequence per batch row
-    // ordered look-back of the chunk-state launch that also passes the states
-    // on (zeroed before the launch): the ticket counter, a status word (bit 0:
-    // a wait gave up) and one flag per (batch, chunk, first head of a block),
-    // set once the state leaving that chunk is published
-    unsigned int* lb_counter;
-    int* lb_status;
-    int* lb_flags;
-    void* states_lo;           // bf16 storage: the residual state - bf16(state) of each published state
-    int lb_spin;               // polls of a flag before its wait gives up; < 0: give up at once
 };
 
 // ---- element traits --------------------------------------------------------

@@ -88,24 +88,14 @@ def test_check_dims_null(lib):
     assert lib.ssd_workspace_size(None) == 0
 
 
-def _round256(v):
-    return (v + 255) // 256 * 256
-
-
 def test_workspace_size(lib):
     d = dims()
     nc = 2
     cs = 2 * 8 * nc * 256 * 4
     st = 2 * nc * 8 * 64 * 128 * 4
-    # look-back scratch: counter, status and one flag per (batch, chunk, head),
-    # then (bf16 storage) the residuals of the published states
-    hdr = _round256((2 + 2 * nc * 8) * 4)
-    assert ssd.ssd_lookback_scratch_size(d) == hdr
-    assert ssd.ssd_workspace_size(d) == hdr + cs + st
+    assert ssd.ssd_workspace_size(d) == cs + st
     assert ssd.ssd_stage_sizes(d) == (cs, st)
-    assert ssd.ssd_lookback_scratch_size(dims(state_dtype="bf16")) == hdr + st // 2
-    assert ssd.ssd_workspace_size(dims(state_dtype="bf16")) == hdr + st // 2 + cs + st // 2
-    assert ssd.ssd_lookback_scratch_size(dims(batch=0)) == 0 and ssd.ssd_lookback_scratch_size(dims(headdim=48)) == 0
+    assert ssd.ssd_workspace_size(dims(state_dtype="bf16")) == cs + st // 2
     assert ssd.ssd_workspace_size(dims(headdim=48)) == 0
     assert ssd.ssd_workspace_size(dims(batch=0)) == 0
     # monotonic in every size
@@ -139,26 +129,6 @@ def test_forward_argument_errors(lib):
     assert f(P(bad), x, dt, A, B, C, D, y, fin, work, ws, None) == SHAPE
     # batch == 0 is a no-op that succeeds without touching any pointer
     assert f(P(dims(batch=0)), None, None, None, None, None, None, None, None, None, 0, None) == OK
-
-
-def test_chunk_state_passing_argument_errors(lib):
-    d = dims()
-    P = ctypes.byref
-    a = _fake(0x300000)
-    n = ssd.ssd_lookback_scratch_size(d)
-    f = lib.ssd_chunk_state_passing
-    assert f(P(d), None, a, a, a, None, a, a, a, a, n, None) == NULLP
-    assert f(P(d), a, a, a, a, None, a, a, a, None, n, None) == NULLP
-    assert f(P(d), a, a, a, a, None, a, a, None, a, n, None) == NULLP
-    assert f(P(d), a, a, a, a, None, a, a, a, _fake(0x300008), n, None) == MISAL
-    assert f(P(d), a, a, a, a, _fake(0x300004), a, a, a, a, n, None) == MISAL
-    assert f(P(d), a, a, a, a, None, a, a, a, a, n - 1, None) == WS
-    assert f(P(dims(ngroups=3)), a, a, a, a, None, a, a, a, a, n, None) == SHAPE
-    assert f(P(dims(batch=0)), None, None, None, None, None, None, None, None, None, 0, None) == OK
-    st = ctypes.c_int32(0)
-    assert lib.ssd_lookback_status(None, P(st), None) == NULLP
-    assert lib.ssd_lookback_status(a, None, None) == NULLP
-    assert lib.ssd_lookback_status(_fake(0x300004), P(st), None) == MISAL
 
 
 def test_stage_argument_errors(lib):

@@ -101,50 +101,28 @@ def test_resume_from_prefix_final_state(state_dtype):
     assert ey <= TOL[w.dtype] and ef <= TOL[w.dtype]
 
 
-@pytest.mark.parametrize("state_dtype", ["fp32", "bf16"])
-def test_stage_entry_points_with_initial_state(state_dtype):
-    """ssd_forward_init is bitwise the chunk-state launch with the state passing
-    folded in (from the initial state) followed by ssd_chunk_scan_init; with
-    fp32 storage also bitwise the three single stages (cumsum+state, state
-    passing from the initial state, chunk scan), with bf16 storage within the
-    tolerance of them."""
+def test_stage_entry_points_with_initial_state():
+    """cumsum+state, state passing and chunk scan from an initial state, one by
+    one, give bitwise what ssd_forward_init gives."""
     w = workload("m125", batch=1, seqlen=600, nheads=4)
     g = to_dev(inputs.generate_slow_decay(w, seed=36))
     init = inputs.generate_initial_state(w, seed=36).to("cuda")
-    d = ssd.dims_of(g["x"], g["B"], w.chunk_size, state_dtype)
+    d = ssd.dims_of(g["x"], g["B"], w.chunk_size, "bf16")
     b, H, P, N, nc, Q = d.batch, d.nheads, d.headdim, d.dstate, d.nchunks, d.chunk_size
-    sdt = torch.bfloat16 if state_dtype == "bf16" else torch.float32
-    # the single stages
     cs = torch.empty((b, H, nc, Q), device="cuda")
-    states = torch.empty((b, nc, H, P, N), dtype=sdt, device="cuda")
+    states = torch.empty((b, nc, H, P, N), dtype=torch.bfloat16, device="cuda")
     fin = torch.empty((b, H, N, P), device="cuda")
     y = torch.empty_like(g["x"])
     ssd.ssd_chunk_cumsum_state(d, g["x"], g["dt"], g["A"], g["B"], cs, states)
     ssd.ssd_state_passing_init(d, cs, states, init, fin)
     ssd.ssd_chunk_scan_init(d, g["x"], g["dt"], g["B"], g["C"], g["D"], cs, states, y)
-    # the two launches of the forward
-    cs2 = torch.empty_like(cs)
-    states2 = torch.empty_like(states)
-    fin2 = torch.empty_like(fin)
-    y2 = torch.empty_like(y)
-    n = ssd.ssd_lookback_scratch_size(d)
-    scratch = torch.empty(n, dtype=torch.uint8, device="cuda")
-    ssd.ssd_chunk_state_passing(d, g["x"], g["dt"], g["A"], g["B"], init, cs2, states2, fin2, scratch, n)
-    ssd.ssd_chunk_scan_init(d, g["x"], g["dt"], g["B"], g["C"], g["D"], cs2, states2, y2)
-    y3, fin3 = ssd.forward(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], w.chunk_size, state_dtype,
+    y2, fin2 = ssd.forward(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], w.chunk_size, "bf16",
                            initial_state=init)
     torch.cuda.synchronize()
-    assert ssd.ssd_lookback_status(scratch) == 0
-    assert torch.equal(y2, y3) and torch.equal(fin2, fin3)
-    if state_dtype == "fp32":
-        assert torch.equal(y, y2) and torch.equal(fin, fin2) and torch.equal(states, states2)
-    else:
-        tol = TOL[w.dtype]
-        assert oracle.rel_err(y2.float().cpu().numpy(), y.float().cpu().numpy()) <= tol
-        assert oracle.rel_err(fin2.cpu().numpy(), fin.cpu().numpy()) <= tol
-    # h_0 as stored for the chunk scan is the initial state ([P][N], storage type)
-    h0 = states2[:, 0].float().transpose(-1, -2)
-    assert torch.equal(h0, init.to(sdt).float())
+    assert torch.equal(y, y2) and torch.equal(fin, fin2)
+    # h_0 as stored for the chunk scan is the initial state ([P][N], bf16)
+    h0 = states[:, 0].float().transpose(-1, -2)
+    assert torch.equal(h0, init.to(torch.bfloat16).float())
 
 
 def test_empty_sequence_copies_initial_state():
