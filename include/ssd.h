@@ -69,7 +69,8 @@ typedef enum {
     SSD_ERR_UNSUPPORTED = 3,         /* headdim/dstate/chunk_size/dtype outside the lists above */
     SSD_ERR_MISALIGNED = 4,          /* a tensor pointer is not 16-byte aligned */
     SSD_ERR_WORKSPACE_TOO_SMALL = 5, /* workspace_bytes < ssd_workspace_size() */
-    SSD_ERR_LAUNCH = 6               /* the HIP runtime rejected a launch */
+    SSD_ERR_LAUNCH = 6,              /* the HIP runtime rejected a launch */
+    SSD_ERR_TOO_LARGE = 7            /* ssd_forward_noalloc: the workspace would exceed its fixed scratch */
 } ssd_status;
 
 typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
@@ -122,6 +123,29 @@ ssd_status ssd_forward(const ssd_dims* d, const void* x, const float* dt, const 
                        const void* B, const void* C, const float* D, void* y,
                        float* final_state, void* workspace, size_t workspace_bytes,
                        hipStream_t stream);
+
+/*
+ * ssd_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same launches and results as ssd_forward, with the workspace kept in a
+ * fixed device array inside the library (ssd_noalloc_scratch_bytes() bytes,
+ * 64 MiB) instead of a caller buffer. Each GPU the call runs on holds its own
+ * copy of that array until the process ends; its address is looked up once per
+ * device on the first call there. The call itself allocates nothing. Every
+ * call on one GPU shares that GPU's array, so calls that overlap in time on
+ * one GPU (other streams, other threads) race and must be serialised by the
+ * caller; the array's contents on entry do not matter (nothing is read before
+ * it is written). Errors: as ssd_forward (without the workspace ones), plus
+ * SSD_ERR_TOO_LARGE when ssd_workspace_size(d) exceeds the array, and
+ * SSD_ERR_LAUNCH when the array's device address cannot be found.
+ */
+ssd_status ssd_forward_noalloc(const ssd_dims* d, const void* x, const float* dt, const float* A,
+                               const void* B, const void* C, const float* D, void* y,
+                               float* final_state, hipStream_t stream);
+
+/* Bytes of the fixed device scratch of ssd_forward_noalloc (the largest
+ * ssd_workspace_size it accepts). */
+size_t ssd_noalloc_scratch_bytes(void);
 
 /*
  * Full forward from a given initial state: the recurrence of Knowl 1 started

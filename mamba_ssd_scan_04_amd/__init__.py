@@ -86,6 +86,9 @@ def load_library() -> ctypes.CDLL:
     lib.ssd_chunk_scan_init.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.ssd_chunk_scan_init.restype = st
     lib.ssd_step.argtypes, lib.ssd_step.restype = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp], st
+    lib.ssd_forward_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.ssd_forward_noalloc.restype = st
+    lib.ssd_noalloc_scratch_bytes.argtypes, lib.ssd_noalloc_scratch_bytes.restype = [], sz
     _lib = lib
     return lib
 
@@ -255,6 +258,19 @@ def ssd_forward(d, x, dt, A, B, C, D, y, final_state, workspace, workspace_bytes
     _check(load_library().ssd_forward(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
                                       _ptr(C), _ptr(D), _ptr(y), _ptr(final_state),
                                       _ptr(workspace), workspace_bytes, s))
+
+
+def ssd_forward_noalloc(d, x, dt, A, B, C, D, y, final_state, stream=None):
+    """ssd_forward with the workspace in the library's fixed device scratch
+    (no allocation); calls on one GPU must not overlap."""
+    _check_io(d, x=x, dt=dt, A=A, B=B, C=C, D=D, y=y, final_state=final_state)
+    s = _stream(x.device) if stream is None else stream
+    _check(load_library().ssd_forward_noalloc(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
+                                              _ptr(D), _ptr(y), _ptr(final_state), s))
+
+
+def ssd_noalloc_scratch_bytes() -> int:
+    return load_library().ssd_noalloc_scratch_bytes()
 
 
 def ssd_forward_init(d, x, dt, A, B, C, D, initial_state, y, final_state, workspace, workspace_bytes,

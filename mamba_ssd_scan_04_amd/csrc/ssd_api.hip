@@ -89,6 +89,9 @@ const char* ssd_status_string(ssd_status s) {
         case SSD_ERR_MISALIGNED: return "a tensor pointer is not 16-byte aligned";
         case SSD_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than ssd_workspace_size()";
         case SSD_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
+        case SSD_ERR_TOO_LARGE:
+            return "the workspace this problem needs exceeds the library's fixed device scratch "
+                   "(ssd_forward_noalloc handles up to ssd_noalloc_scratch_bytes() of workspace)";
     }
     return "unknown status";
 }
@@ -304,6 +307,56 @@ ssd_status ssd_forward(const ssd_dims* d, const void* x, const float* dt, const 
                        float* final_state, void* workspace, size_t workspace_bytes,
                        hipStream_t stream) {
     return forward_impl(d, x, dt, A, B, C, D, nullptr, nullptr, y, final_state, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---- the allocation-free forward -------------------------------------------
+//
+// The workspace of ssd_forward (cs and the inter-chunk states) in a fixed
+// device array instead of a caller buffer. Each device holds its own copy
+// from the first call on it until the process ends. In host code the array's
+// name is only a stand-in: its device address is looked up once per device
+// (hipGetSymbolAddress) and that address is what the kernels receive.
+constexpr size_t kNoallocScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> scratch_ptr[kMaxDevices];
+
+// this device's address of `scratch`, looked up on its first use (racing
+// first calls look up the same address); nullptr on failure
+void* device_scratch() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    void* p = scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    void* q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) return nullptr;
+    scratch_ptr[dev].store(q, std::memory_order_release);
+    return q;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ssd_noalloc_scratch_bytes(void) { return kNoallocScratchBytes; }
+
+ssd_status ssd_forward_noalloc(const ssd_dims* d, const void* x, const float* dt, const float* A, const void* B,
+                               const void* C, const float* D, void* y, float* final_state, hipStream_t stream) {
+    const ssd_status st = ssd_check_dims(d);
+    if (st != SSD_OK) return st;
+    const size_t need = ssd_workspace_size(d);
+    if (need > kNoallocScratchBytes) return SSD_ERR_TOO_LARGE;
+    if (d->batch == 0) return SSD_OK;
+    if (d->seqlen == 0) return forward_impl(d, x, dt, A, B, C, D, nullptr, nullptr, y, final_state, nullptr, 0, stream);
+    if (!x || !dt || !A || !B || !C || !D || !y || !final_state) return SSD_ERR_NULL_POINTER;
+    void* ws = device_scratch();
+    if (!ws) return SSD_ERR_LAUNCH;
+    return forward_impl(d, x, dt, A, B, C, D, nullptr, nullptr, y, final_state, ws, kNoallocScratchBytes, stream);
 }
 
 ssd_status ssd_step(const ssd_dims* d, const void* x, const float* dt, const float* A, const void* B,

@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
 
 def test_version_and_strings(lib):
     assert ssd.ssd_abi_version() == 1
-    for code in range(7):
+    for code in range(8):
         assert len(ssd.ssd_status_string(code)) > 0
     assert "unknown" in ssd.ssd_status_string(99)
 
@@ -355,3 +355,23 @@ def test_check_dims_rejects_chunk_spans_past_31_bits(lib):
                                    chunk_size=256)) == UNSUP
     assert ssd.ssd_check_dims(dims(dtype="fp32", nheads=8191, ngroups=8191, headdim=16, dstate=256,
                                    chunk_size=256)) == OK
+
+
+def test_noalloc_forward_argument_errors(lib):
+    """The allocation-free forward checks its arguments and its size limit
+    before any HIP call: dims, the fixed scratch's size, then pointers."""
+    P = ctypes.byref
+    a = _fake(0x400000)
+    f = lib.ssd_forward_noalloc
+    assert ssd.ssd_noalloc_scratch_bytes() == 64 << 20
+    assert "fixed device scratch" in ssd.ssd_status_string(7)
+    d = dims()   # 2 x 512 tokens, 8 heads of 64 x 128: well under 64 MiB of workspace
+    assert ssd.ssd_workspace_size(d) <= ssd.ssd_noalloc_scratch_bytes()
+    assert f(P(d), None, a, a, a, a, a, a, a, None) == NULLP
+    assert f(P(d), a, a, a, a, a, a, a, None, None) == NULLP
+    assert f(P(dims(ngroups=3)), a, a, a, a, a, a, a, a, None) == SHAPE
+    assert f(P(dims(headdim=48)), a, a, a, a, a, a, a, a, None) == UNSUP
+    big = dims(batch=8, seqlen=4096, nheads=80)   # the 2.7B-layer shape: ~346 MB of fp32 states
+    assert ssd.ssd_workspace_size(big) > ssd.ssd_noalloc_scratch_bytes()
+    assert f(P(big), a, a, a, a, a, a, a, a, None) == 7
+    assert f(P(dims(batch=0)), None, None, None, None, None, None, None, None, None) == OK
