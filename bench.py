@@ -40,7 +40,7 @@ MFMA_F32_PEAK_TFS = 157.3
 # kernel with the in-chunk prefix sums formed inside it
 KERNELS = ["ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan"]
 SOURCES = {"ssd_chunk_cumsum": "chunk_cumsum.hip", "ssd_chunk_state": "chunk_state.hip",
-           "ssd_state_passing": "state_passing.hip", "ssd_chunk_scan": "chunk_scan.hip"}
+           "ssd_state_passing": "state_passing.hip", "ssd_chunk_scan": "chunk_scan_impl.hpp"}
 
 
 def kernel_work(w, state_bytes: int) -> dict:
@@ -568,14 +568,27 @@ def main() -> int:
     sB, sC = g["B"][:, 0].contiguous(), g["C"][:, 0].contiguous()
     sstate = torch.zeros((w.batch, w.nheads, w.dstate, w.headdim), dtype=torch.float32, device=dev)
     sy = torch.empty_like(sx)
+    # the binding checks the arguments once; the timed loop then calls the C
+    # entry point directly, so that the host's per-call work (microseconds of
+    # Python) does not starve a kernel that takes a few microseconds
+    ssd.ssd_step(dstep, sx, sdt, g["A"], sB, sC, g["D"], sstate, sy, sh)
+    import ctypes
+    step_fn = ssd.load_library().ssd_step
+    step_args = (ctypes.byref(dstep), *(t.data_ptr() for t in (sx, sdt, g["A"], sB, sC, g["D"], sstate, sy)), sh)
+
+    def decode_step():
+        rc = step_fn(*step_args)
+        if rc != 0:
+            raise ssd.SsdError(rc)
+
     for _ in range(args.warmup):
-        ssd.ssd_step(dstep, sx, sdt, g["A"], sB, sC, g["D"], sstate, sy, sh)
+        decode_step()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     nstep = 200
     torch.cuda.synchronize()
     e0.record(stream)
     for _ in range(nstep):
-        ssd.ssd_step(dstep, sx, sdt, g["A"], sB, sC, g["D"], sstate, sy, sh)
+        decode_step()
     e1.record(stream)
     torch.cuda.synchronize()
     step_us = e0.elapsed_time(e1) * 1e3 / nstep

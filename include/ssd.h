@@ -35,7 +35,7 @@
  *    computed as written (the pages take a_t in [0, 1]).
  *  - Sizes: batch >= 0, seqlen >= 0 (0 gives a zero final state), nheads,
  *    ngroups >= 1 with nheads % ngroups == 0; headdim P in {16, 32, 64, 128};
- *    dstate N in {16, 32, 64, 128, 256}; chunk_size Q in {32, 64, 128, 256}.
+ *    dstate N in {16, 32, 64, 128, 256}; chunk_size Q in {16, 32, 64, 128, 256}.
  *    seqlen need not be a multiple of Q: the last chunk may be shorter.
  *
  * Tensor layouts (b = batch, T = seqlen, H = nheads, P = headdim, N = dstate,

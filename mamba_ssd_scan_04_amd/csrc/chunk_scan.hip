@@ -31,6 +31,7 @@ hipError_t launch_chunk_scan(const Params& p, int dtype, int state_dtype, hipStr
 // x and h_c buffers; used by argument checking.
 int chunk_scan_lds_bytes(int dtype, int state_dtype, int64_t P, int64_t N, int64_t Q) {
     const int esz = dtype == 1 ? 2 : 4, ssz = state_dtype == 1 ? 2 : 4;
+    if (Q < 32) Q = 32;   // rows as tiled: whole 32-token tiles
     const int pp = (int)((P + 31) / 32) * 32, np = (int)((N + 31) / 32) * 32;
     return (int)Q * pp * esz + pp * np * ssz + 2 * 3 * (int)Q * 4;
 }

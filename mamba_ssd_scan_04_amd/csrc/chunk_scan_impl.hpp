@@ -96,12 +96,16 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
     constexpr int KS = Cfg::KS, XRC = Cfg::XRC, HRC = Cfg::HRC;
     constexpr int ESZ = (int)sizeof(T), SSZ = (int)sizeof(ST);
     extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+    // Q: tokens per chunk (the stride of chunks and of cs rows); QT: the
+    // chunk's rows as tiled, whole 32-token tiles (Q = 16 fills half a tile,
+    // whose other rows are masked like the tail of a short last chunk)
     const int Q = (int)p.chunk;
-    const int XB = Cfg::xbytes(Q), VB = Cfg::vbytes(Q);
+    const int QT = Q < 32 ? 32 : Q;
+    const int XB = Cfg::xbytes(QT), VB = Cfg::vbytes(QT);
     unsigned char* const hb0 = smem + NBX * XB;
     float* const vb0 = reinterpret_cast<float*>(hb0 + NBH * Cfg::HBYTES);
     unsigned char* const cbl0 = reinterpret_cast<unsigned char*>(vb0) + 2 * VB;   // C B^T tiles (CBL)
-    int* const sqv = reinterpret_cast<int*>(cbl0 + (CBL ? Cfg::cbbytes(Q) : 0));    // document ids (VARLEN)
+    int* const sqv = reinterpret_cast<int*>(cbl0 + (CBL ? Cfg::cbbytes(QT) : 0));   // document ids (VARLEN)
 
     // ---- block coordinates (uniform) ----
     const int64_t T_ = p.seqlen, H = p.nheads, P = p.headdim, N = p.dstate, G = p.ngroups;
@@ -130,7 +134,7 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
     const int hf = lane >> 5, l32 = lane & 31;
     // Row tile of this wavefront. Waves w and w+4 share a SIMD; with 8 tiles
     // they take tiles s and 7 - s, so every SIMD carries 9 key tiles of work.
-    const int RT = Q / 32;
+    const int RT = QT / 32;
     const int rt = RT == 8 ? (wave < 4 ? wave : 11 - wave) : (wave < RT ? wave : -1);
     const bool active = rt >= 0;
     // the heavier row tiles (the longer chain of key tiles per head) get issue
@@ -152,7 +156,7 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
     constexpr int NIX = (256 * XRC / 64 + kScanWaves - 1) / kScanWaves;
     constexpr int NIH = (PT * 32 * HRC / 64 + kScanWaves - 1) / kScanWaves;
     int offx[NIX], offh[NIH];
-    dma_tile_plan<XRC, NIX>(offx, Q, qc, xvalid, xstride, wave, kScanWaves, lane);
+    dma_tile_plan<XRC, NIX>(offx, QT, qc, xvalid, xstride, wave, kScanWaves, lane);
     dma_tile_plan<HRC, NIH>(offh, PT * 32, (int)P, hvalid, (uint32_t)(N * SSZ), wave, kScanWaves, lane);
     auto issue_x = [&](int hh, unsigned char* dst) {
         dma_tile_issue<NIX>(dst, xbase + (int64_t)hh * hs * P * ESZ, offx, wave, kScanWaves);
@@ -161,35 +165,37 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
         dma_tile_issue<NIH>(dst, sbase + (int64_t)hh * hs * P * N * SSZ, offh, wave, kScanWaves);
     };
     float vcs = 0.0f, vcr = 0.0f, vdt = 0.0f;   // thread i holds token i of the next head
-    // packed documents: thread i < Q holds the id of token i (clamped to the
+    // packed documents: thread i < QT holds the id of token i (clamped to the
     // chunk); sprev is the id of the token before the chunk (the first token's
     // for chunk 0, whose carried state is the initial one)
     int vsq = 0, sprev = 0;
     if constexpr (VARLEN) {
         const int* sq = p.seq_idx + b * T_;
         sprev = sq[c > 0 ? t0 - 1 : 0];
-        if ((int)threadIdx.x < Q) vsq = sq[t0 + min((int)threadIdx.x, qc - 1)];
+        if ((int)threadIdx.x < QT) vsq = sq[t0 + min((int)threadIdx.x, qc - 1)];
     }
+    // rows past the chunk's Q tokens (Q = 16) take its last cs value, as the
+    // padding of a short last chunk does
     auto load_vec = [&](int hh) {
         const int i = threadIdx.x;
-        if (i < Q) {
+        if (i < QT) {
             const float* csr = csbase + (int64_t)hh * hs * nc * Q;
-            vcs = ldg(csr + i);
-            vcr = ldg(csr + (i | 31));
+            vcs = ldg(csr + min(i, Q - 1));
+            vcr = ldg(csr + min(i | 31, Q - 1));
             vdt = (i < qc) ? ldg(dtbase + hh * hs + (uint32_t)i * (uint32_t)H) : 0.0f;
         }
     };
-    // per-head vectors in LDS, token i of the chunk (log2 units: c2 = cs log2 e):
-    //   [0, Q)   c2_i                            (2^c2_j is the carried-state row scale)
-    //   [Q, 2Q)  2^(c2_r - c2_i) dt_i, r = the last token of i's 32-token tile
-    //   [2Q,3Q)  dt_i                            (0 past the chunk's end)
+    // per-head vectors in LDS, token i of the chunk's tiles (log2 units: c2 = cs log2 e):
+    //   [0, QT)    c2_i                            (2^c2_j is the carried-state row scale)
+    //   [QT, 2QT)  2^(c2_r - c2_i) dt_i, r = the last token of i's 32-token tile
+    //   [2QT,3QT)  dt_i                            (0 past the chunk's end)
     auto store_vec = [&](float* v) {
         const int i = threadIdx.x;
-        if (i < Q) {
+        if (i < QT) {
             const float c2 = vcs * kLog2e, c2r = vcr * kLog2e;
             v[i] = c2;
-            v[Q + i] = exp2f(c2r - c2) * vdt;
-            v[2 * Q + i] = vdt;
+            v[QT + i] = exp2f(c2r - c2) * vdt;
+            v[2 * QT + i] = vdt;
         }
     };
 
@@ -319,7 +325,7 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
 
     if (nh > 0) store_vec(vb0);
     if constexpr (VARLEN) {
-        if ((int)threadIdx.x < Q) sqv[threadIdx.x] = vsq;
+        if ((int)threadIdx.x < QT) sqv[threadIdx.x] = vsq;
     }
     wait_vmem();
     lds_barrier();
@@ -358,8 +364,8 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
         }
         bool stored_all = true;
         if (active) {
-            const float* uv = c2v + Q;
-            const float* dtv = c2v + 2 * Q;
+            const float* uv = c2v + QT;
+            const float* dtv = c2v + 2 * QT;
             int jl = rt * 32 + l32, qch = qc;
             asm volatile("" : "+v"(jl), "+v"(qch));    // keep per-element compares in the loop
             // The products are formed transposed, Y^T = X^T M^T (+ h^T C^T): the
@@ -661,7 +667,7 @@ static inline int scan_hpw(const Params& p) {
 template <typename T, int PT, int NT, typename ST, int VAR>
 static hipError_t launch_sc(const Params& p, hipStream_t s) {
     using Cfg = ScanCfg<T, PT, NT, ST>;
-    const int Q = (int)p.chunk;
+    const int Q = p.chunk < 32 ? 32 : (int)p.chunk;   // rows as tiled (whole 32-token tiles)
     const int hpw = scan_hpw(p);
     // prefer C B^T in LDS (frees the registers that would hold it), then
     // double-buffered copies

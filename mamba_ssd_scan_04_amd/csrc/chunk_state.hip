@@ -104,9 +104,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     constexpr int ESZ = (int)sizeof(T);
     __shared__ __attribute__((aligned(1024))) unsigned char smem[Cfg::LDS];
     constexpr int NBUF = Cfg::NBUF;
-    float* wv = reinterpret_cast<float*>(smem + NBUF * Cfg::BUF);   // [HPW][Q]: dt, then w
+    float* wv = reinterpret_cast<float*>(smem + NBUF * Cfg::BUF);   // [HPW][QT]: dt, then w
 
+    // Q: tokens per chunk; QT: its rows as tiled, whole 32-token blocks (a
+    // 16-token chunk fills half a block, whose other rows get weight 0)
     const int Q = (int)p.chunk;
+    const int QT = Q < kStateKB ? kStateKB : Q;
     const int64_t T_ = p.seqlen, H = p.nheads, P = p.headdim, N = p.dstate, G = p.ngroups;
     const int64_t hpg = p.heads_per_group, nc = p.nchunks;
     const int nhb = (int)((hpg + HPW - 1) / HPW);
@@ -137,12 +140,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     int offb[Cfg::NDB], offx[Cfg::NDX];
     dma_plan<Cfg::BRC, Cfg::NDB>(offb, bvalid, bstride, wave, lane);
     dma_plan<Cfg::XRC, Cfg::NDX>(offx, xvalid, xstride, wave, lane);
-    // side tile: lane value fi = (wave + 4i) * 64 + lane is (head fi / Q, token fi % Q)
-    const int srounds = (HPW * Q + 255) / 256;
+    // side tile: lane value fi = (wave + 4i) * 64 + lane is (head fi / QT, token fi % QT)
+    const int srounds = (HPW * QT + 255) / 256;
     auto issue_side = [&]() {
         const __amdgpu_buffer_rsrc_t rd = raw_rsrc(dtbase);
         for (int i = 0; i < srounds; ++i) {
-            const int fi = (wave + 4 * i) * 64 + lane, hq = fi / Q, j = fi - hq * Q;
+            const int fi = (wave + 4 * i) * 64 + lane, hq = fi / QT, j = fi - hq * QT;
             const bool ok = hq < nh && j < qc;
             dma4(rd, ok ? (uint32_t)(j * (int)H + hq) * 4u : kOob, reinterpret_cast<unsigned char*>(wv) + fi * 4);
         }
@@ -192,7 +195,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int i = 0; i < Cfg::NDX; ++i) nx += ((wave + 4 * i) * 64 < kStateKB * Cfg::XRC) ? 1 : 0;
     const int per_block = nb + nh * nx;
 
-    const int nblk = Q / kStateKB;
+    const int nblk = QT / kStateKB;
     constexpr int AHEAD = NBUF - 1;     // blocks in flight beyond the one in use
     const int hq = wave / WPH;   // = hh: the head this wavefront computes w for
     float Ah = 0.0f;
@@ -211,7 +214,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int per = Q >= 64 ? Q / 64 : 1, nact = Q / per;
     float csv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     if (wave % WPH == 0) {
-        float* row = wv + hq * Q;
+        float* row = wv + hq * QT;
         float dtv[4], v[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) dtv[k] = (k < per && lane < nact) ? row[lane * per + k] : 0.0f;
@@ -299,7 +302,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     };
     for (int blk = 0; blk < nblk; ++blk) {
         step(blk, smem + (blk % NBUF) * Cfg::BUF, smem + ((blk + AHEAD) % NBUF) * Cfg::BUF,
-             wv + hh * Q + blk * kStateKB);
+             wv + hh * QT + blk * kStateKB);
         // block blk+1 must have landed; later blocks may still be in flight
         const int later = min(AHEAD - 1, nblk - 2 - blk);
         wait_vmem_le_rt(later > 0 ? later * per_block : 0);

@@ -83,7 +83,7 @@ const char* ssd_status_string(ssd_status s) {
         case SSD_ERR_BAD_SHAPE: return "bad shape: negative or zero size, or nheads not divisible by ngroups";
         case SSD_ERR_UNSUPPORTED:
             return "unsupported configuration: headdim in {16,32,64,128}, dstate in {16,32,64,128,256}, "
-                   "chunk_size in {32,64,128,256}, dtype fp32/bf16, bf16 states only with bf16 inputs, "
+                   "chunk_size in {16,32,64,128,256}, dtype fp32/bf16, bf16 states only with bf16 inputs, "
                    "the chunk scan's x and state tiles must fit in LDS (Q*P*esize + P*N*ssize <= ~156 KB), "
                    "and one chunk's rows must span less than 2^31 bytes (Q*H*P*esize, Q*G*N*esize)";
         case SSD_ERR_MISALIGNED: return "a tensor pointer is not 16-byte aligned";
@@ -99,13 +99,13 @@ const char* ssd_status_string(ssd_status s) {
 ssd_status ssd_check_dims(const ssd_dims* d) {
     static const int64_t kP[] = {16, 32, 64, 128};
     static const int64_t kN[] = {16, 32, 64, 128, 256};
-    static const int64_t kQ[] = {32, 64, 128, 256};
+    static const int64_t kQ[] = {16, 32, 64, 128, 256};
     if (!d) return SSD_ERR_NULL_POINTER;
     if (d->batch < 0 || d->seqlen < 0 || d->nheads <= 0 || d->headdim <= 0 || d->dstate <= 0 ||
         d->ngroups <= 0 || d->chunk_size <= 0)
         return SSD_ERR_BAD_SHAPE;
     if (d->nheads % d->ngroups != 0) return SSD_ERR_BAD_SHAPE;
-    if (!in_list(d->headdim, kP, 4) || !in_list(d->dstate, kN, 5) || !in_list(d->chunk_size, kQ, 4))
+    if (!in_list(d->headdim, kP, 4) || !in_list(d->dstate, kN, 5) || !in_list(d->chunk_size, kQ, 5))
         return SSD_ERR_UNSUPPORTED;
     if (d->dtype != SSD_F32 && d->dtype != SSD_BF16) return SSD_ERR_UNSUPPORTED;
     if (d->state_dtype != SSD_F32 && d->state_dtype != SSD_BF16) return SSD_ERR_UNSUPPORTED;
@@ -421,7 +421,7 @@ ssd_status ssd_forward_varlen(const ssd_dims* d, const void* x, const float* dt,
     if (reinterpret_cast<uintptr_t>(seq_idx) & 3) return SSD_ERR_MISALIGNED;
     // the chunk scan keeps the chunk's document ids in LDS beside its tiles
     if (ssd::chunk_scan_lds_bytes(d->dtype, d->state_dtype, d->headdim, d->dstate, d->chunk_size) +
-            4 * d->chunk_size > kMaxLds)
+            4 * (d->chunk_size < 32 ? 32 : d->chunk_size) > kMaxLds)
         return SSD_ERR_UNSUPPORTED;
     return forward_impl(d, x, dt, A, B, C, D, initial_state, nullptr, y, final_state, workspace, workspace_bytes,
                         stream, seq_idx);

@@ -64,7 +64,8 @@ def dims(**kw):
     (dict(headdim=256), UNSUP),
     (dict(dstate=8), UNSUP),
     (dict(dstate=512), UNSUP),
-    (dict(chunk_size=16), UNSUP),
+    (dict(chunk_size=16), OK),
+    (dict(chunk_size=8), UNSUP),
     (dict(chunk_size=100), UNSUP),
     (dict(dtype=7), UNSUP),
     (dict(state_dtype=5), UNSUP),

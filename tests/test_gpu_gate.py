@@ -17,6 +17,7 @@ pytestmark = pytest.mark.gpu
     ("tiny", dict(batch=2, seqlen=333, nheads=3, headdim=64, dstate=128, chunk_size=128), "fp32", True),
     ("m125", dict(batch=2, seqlen=1000, nheads=4), "bf16", False),
     ("m125", dict(batch=1, seqlen=520, nheads=3, headdim=16, dstate=256, chunk_size=64), "fp32", True),
+    ("m125", dict(batch=1, seqlen=200, nheads=2, chunk_size=16), "bf16", True),
 ])
 def test_gated_forward(name, kw, state_dtype, with_init):
     w = workload(name, **kw)

@@ -49,7 +49,7 @@ def test_m125_shape_ragged_with_initial_state(state_dtype):
     check(w, inputs.generate_slow_decay(w, seed=31), inputs.generate_initial_state(w, seed=31), state_dtype)
 
 
-@pytest.mark.parametrize("Q,T", [(32, 100), (64, 64), (128, 300), (256, 31)])
+@pytest.mark.parametrize("Q,T", [(16, 100), (32, 100), (64, 64), (128, 300), (256, 31)])
 def test_chunk_sizes_with_initial_state(Q, T):
     w = workload("m125", batch=1, seqlen=T, nheads=3, chunk_size=Q)
     check(w, inputs.generate_slow_decay(w, seed=32), inputs.generate_initial_state(w, seed=32))

@@ -49,10 +49,26 @@ def test_slow_decay_inter_chunk_path(state_dtype):
     check(w, inputs.generate_slow_decay(w, seed=2), state_dtype)
 
 
-@pytest.mark.parametrize("Q", [32, 64, 128, 256])
+@pytest.mark.parametrize("Q", [16, 32, 64, 128, 256])
 def test_chunk_sizes(Q):
     w = workload("m125", batch=1, seqlen=600, nheads=2, chunk_size=Q)
     check(w, inputs.generate_slow_decay(w, seed=3))
+
+
+@pytest.mark.parametrize("T", [16, 17, 100, 257])
+@pytest.mark.parametrize("state_dtype", ["fp32", "bf16"])
+def test_chunk_size_16(T, state_dtype):
+    """Q = 16 ("Transformers are SSMs", Knowl 2 takes Q = N = P; N = P = 16 is
+    the tiny shape): each chunk fills half of a 32-token tile, the other half
+    masked like the tail of a short last chunk; ragged T included."""
+    w = workload("m125", batch=2, seqlen=T, nheads=4, headdim=64, dstate=128, chunk_size=16)
+    check(w, inputs.generate_slow_decay(w, seed=31), state_dtype)
+
+
+def test_chunk_size_16_tiny_fp32():
+    """The tiny fp32 shape with Q = N = P = 16."""
+    w = workload("tiny", chunk_size=16)
+    check(w, inputs.generate(w, seed=32))
 
 
 @pytest.mark.parametrize("P,N,state", [(16, 16, "fp32"), (32, 64, "fp32"), (64, 16, "fp32"), (64, 256, "fp32"),
@@ -77,7 +93,7 @@ def test_large_state_tiles(P, N, state, Q):
     check(w, inputs.generate_slow_decay(w, seed=12), state)
 
 
-@pytest.mark.parametrize("P,N,Q", [(16, 16, 64), (64, 128, 128), (32, 32, 32), (64, 64, 256)])
+@pytest.mark.parametrize("P,N,Q", [(16, 16, 64), (64, 128, 128), (32, 32, 32), (64, 64, 256), (16, 16, 16)])
 def test_fp32_inputs(P, N, Q):
     w = workload("tiny", batch=2, seqlen=333, nheads=3, headdim=P, dstate=N, chunk_size=Q)
     check(w, inputs.generate_slow_decay(w, seed=6))
@@ -142,14 +158,14 @@ def test_deterministic_and_fully_written():
 
 
 @pytest.mark.parametrize("state_dtype", ["fp32", "bf16"])
-@pytest.mark.parametrize("T", [900, 16384])
-def test_stage_parity(state_dtype, T):
+@pytest.mark.parametrize("T,Q", [(900, 256), (16384, 256), (900, 16)])
+def test_stage_parity(state_dtype, T, Q):
     """Each stage against its fp64 counterpart: cs against the block algorithm's
     prefix sums, S against its chunk states, h_in against the recurrence's state
     at every chunk boundary, final and y against the recurrence; T = 16384 is a
     chain of 64 chunk states on slow-decay rows, where rounding that compounded
     along the chain would show."""
-    w = workload("m125", batch=2 if T < 4096 else 1, seqlen=T, nheads=3, ngroups=1)
+    w = workload("m125", batch=2 if T < 4096 else 1, seqlen=T, nheads=3, ngroups=1, chunk_size=Q)
     inp = inputs.generate_slow_decay(w, seed=11)
     say(f"stage case {w.describe()} state={state_dtype}")
     dev = to_dev(inp)

@@ -50,7 +50,7 @@ def test_m125_shape_ragged_documents(state_dtype, with_init):
           state_dtype, init)
 
 
-@pytest.mark.parametrize("Q,T", [(32, 100), (64, 64), (128, 300), (256, 31)])
+@pytest.mark.parametrize("Q,T", [(16, 100), (32, 100), (64, 64), (128, 300), (256, 31)])
 def test_chunk_sizes_documents(Q, T):
     w = workload("m125", batch=1, seqlen=T, nheads=3, chunk_size=Q)
     check(w, inputs.generate_slow_decay(w, seed=42), inputs.generate_seq_idx(w, 42, 4, cuts=(Q,)))
