@@ -375,20 +375,33 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
 #pragma unroll
             for (int pt = 0; pt < PT; ++pt) acc[pt] = zero16();
             const float c2j = c2v[jl];
-            // gate inputs of this lane's outputs (token jl, the 4 p of each
-            // accumulator quarter), loaded now and used in the epilogue
+            // gate inputs of this lane's outputs (token jl), loaded now and
+            // used in the epilogue. bf16: 16 bytes per lane in the layout y is
+            // stored in (8 consecutive p of row jl, see the epilogue), turned
+            // into the accumulator's quarters there by the same lane-half swap;
+            // fp32: the 4 p of each accumulator quarter.
             typedef __attribute__((ext_vector_type(4))) T T4;
-            T4 zq[PT][GATE ? 4 : 1];
+            T4 zq[PT][GATE && ESZ == 4 ? 4 : 1];
+            u32x4 z16[PT][GATE && ESZ == 2 ? 2 : 1];
             if constexpr (GATE) {
                 const T* zr = static_cast<const T*>(p.z) +
                               ((tok0 + min(jl, qch - 1)) * H + h0 + (int64_t)hh * hs) * P;
 #pragma unroll
-                for (int pt = 0; pt < PT; ++pt)
+                for (int pt = 0; pt < PT; ++pt) {
+                    if constexpr (ESZ == 2) {
 #pragma unroll
-                    for (int gq = 0; gq < 4; ++gq) {
-                        const int p0 = min(pt * 32 + 8 * gq + 4 * hf, (int)P - 4);
-                        zq[pt][gq] = *(const __attribute__((address_space(1))) T4*)(zr + p0);
+                        for (int gp = 0; gp < 2; ++gp) {
+                            const int p0 = min(pt * 32 + 8 * (2 * gp + hf), (int)P - 8);
+                            z16[pt][gp] = *(const __attribute__((address_space(1))) u32x4*)(zr + p0);
+                        }
+                    } else {
+#pragma unroll
+                        for (int gq = 0; gq < 4; ++gq) {
+                            const int p0 = min(pt * 32 + 8 * gq + 4 * hf, (int)P - 4);
+                            zq[pt][gq] = *(const __attribute__((address_space(1))) T4*)(zr + p0);
+                        }
                     }
+                }
             }
             // y * silu(z) = y z / (1 + 2^(-z log2 e)), with the hardware exp2 and
             // reciprocal (z -> -inf gives z * rcp(inf) = -0, z -> +inf gives z)
@@ -535,16 +548,32 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
 #pragma unroll
                     for (int gp = 0; gp < 2; ++gp) {
                         uint32_t w[2][2];
+                        // gate: the row-layout z piece back into quarters 2gp, 2gp+1
+                        uint32_t zw[2][2] = {{0u, 0u}, {0u, 0u}};
+                        if constexpr (GATE) {
+                            zw[0][0] = z16[pt][gp][0]; zw[0][1] = z16[pt][gp][1];
+                            zw[1][0] = z16[pt][gp][2]; zw[1][1] = z16[pt][gp][3];
+#pragma unroll
+                            for (int k = 0; k < 2; ++k) {
+                                const auto sw = __builtin_amdgcn_permlane32_swap(zw[0][k], zw[1][k], false, false);
+                                zw[0][k] = sw[0];
+                                zw[1][k] = sw[1];
+                            }
+                        }
 #pragma unroll
                         for (int q = 0; q < 2; ++q) {
                             const int gq = 2 * gp + q;
                             const int xo = tile_byte<XRC>(jl, (pt * 32 + 8 * gq + 4 * hf) * ESZ);
                             const bf16x4 xv = *reinterpret_cast<const bf16x4*>(xt + xo);
+                            u32x2 zp;
+                            zp[0] = zw[q][0];
+                            zp[1] = zw[q][1];
+                            const bf16x4 zv = __builtin_bit_cast(bf16x4, zp);
                             bf16x4 yv;
 #pragma unroll
                             for (int r = 0; r < 4; ++r) {
                                 const float v = acc[pt][4 * gq + r] + Dh * to_f32(xv[r]);
-                                if constexpr (GATE) yv[r] = from_f32<T>(gate(v, zq[pt][gq][r]));
+                                if constexpr (GATE) yv[r] = from_f32<T>(gate(v, zv[r]));
                                 else yv[r] = from_f32<T>(v);
                             }
                             const u32x2 wv = __builtin_bit_cast(u32x2, yv);
