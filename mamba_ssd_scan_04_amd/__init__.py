@@ -105,6 +105,44 @@ def _check(code: int) -> None:
         raise SsdError(code)
 
 
+# A call of a C entry point, made by the wrappers below after their checks.
+# While `prepared` runs a wrapper, the call is recorded instead of made.
+_recording = None
+
+
+def _launch(name: str, *args):
+    if _recording is not None:
+        _recording.append((getattr(load_library(), name), args))
+        return 0
+    return getattr(load_library(), name)(*args)
+
+
+def prepared(fn, *args, **kwargs):
+    """Run the checks of one call of a C entry-point wrapper (ssd_forward,
+    ssd_chunk_scan, ...) once, and return a function that repeats exactly that
+    call (same tensors, dims and stream) without re-checking: for timing and
+    other hot loops over fixed buffers, where the checks would cost more host
+    time than the kernels take. The tensors must stay alive and unchanged in
+    shape while the returned function is used."""
+    global _recording
+    _recording = []
+    try:
+        fn(*args, **kwargs)
+        calls = _recording
+    finally:
+        _recording = None
+    if len(calls) != 1:
+        raise ValueError(f"{getattr(fn, '__name__', fn)} made {len(calls)} C calls; prepared() takes one")
+    cfn, cargs = calls[0]
+
+    def call():
+        code = cfn(*cargs)
+        if code != 0:
+            raise SsdError(code)
+
+    return call
+
+
 def _ptr(t) -> int | None:
     if t is None:
         return None
@@ -255,7 +293,7 @@ def ssd_forward(d, x, dt, A, B, C, D, y, final_state, workspace, workspace_bytes
     _check_io(d, x=x, dt=dt, A=A, B=B, C=C, D=D, y=y, final_state=final_state)
     _check_workspace(workspace, workspace_bytes, _device_of(x))
     s = _stream(x.device) if stream is None else stream
-    _check(load_library().ssd_forward(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
+    _check(_launch("ssd_forward", ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
                                       _ptr(C), _ptr(D), _ptr(y), _ptr(final_state),
                                       _ptr(workspace), workspace_bytes, s))
 
@@ -265,7 +303,7 @@ def ssd_forward_noalloc(d, x, dt, A, B, C, D, y, final_state, stream=None):
     (no allocation); calls on one GPU must not overlap."""
     _check_io(d, x=x, dt=dt, A=A, B=B, C=C, D=D, y=y, final_state=final_state)
     s = _stream(x.device) if stream is None else stream
-    _check(load_library().ssd_forward_noalloc(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
+    _check(_launch("ssd_forward_noalloc", ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
                                               _ptr(D), _ptr(y), _ptr(final_state), s))
 
 
@@ -278,7 +316,7 @@ def ssd_forward_init(d, x, dt, A, B, C, D, initial_state, y, final_state, worksp
     _check_io(d, x=x, dt=dt, A=A, B=B, C=C, D=D, initial_state=initial_state, y=y, final_state=final_state)
     _check_workspace(workspace, workspace_bytes, _device_of(final_state))
     s = _stream(final_state.device) if stream is None else stream
-    _check(load_library().ssd_forward_init(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
+    _check(_launch("ssd_forward_init", ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
                                            _ptr(C), _ptr(D), _ptr(initial_state), _ptr(y),
                                            _ptr(final_state), _ptr(workspace), workspace_bytes, s))
 
@@ -288,7 +326,7 @@ def ssd_forward_gated(d, x, dt, A, B, C, D, initial_state, z, y, final_state, wo
     _check_io(d, x=x, dt=dt, A=A, B=B, C=C, D=D, initial_state=initial_state, z=z, y=y, final_state=final_state)
     _check_workspace(workspace, workspace_bytes, _device_of(final_state))
     s = _stream(final_state.device) if stream is None else stream
-    _check(load_library().ssd_forward_gated(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
+    _check(_launch("ssd_forward_gated", ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
                                             _ptr(C), _ptr(D), _ptr(initial_state), _ptr(z), _ptr(y),
                                             _ptr(final_state), _ptr(workspace), workspace_bytes, s))
 
@@ -299,7 +337,7 @@ def ssd_forward_varlen(d, x, dt, A, B, C, D, initial_state, seq_idx, y, final_st
               final_state=final_state)
     _check_workspace(workspace, workspace_bytes, _device_of(final_state))
     s = _stream(final_state.device) if stream is None else stream
-    _check(load_library().ssd_forward_varlen(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
+    _check(_launch("ssd_forward_varlen", ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
                                              _ptr(C), _ptr(D), _ptr(initial_state), _ptr(seq_idx), _ptr(y),
                                              _ptr(final_state), _ptr(workspace), workspace_bytes, s))
 
@@ -309,7 +347,7 @@ def ssd_gated_rmsnorm(d, y, z, weight, eps, groups, out, stream=None):
     _expect_all([("y", y, shx, xt), ("z", z, shx, xt), ("out", out, shx, xt),
                  ("weight", weight, (d.nheads * d.headdim,), torch.float32)])
     s = _stream(out.device) if stream is None else stream
-    _check(load_library().ssd_gated_rmsnorm(ctypes.byref(d), _ptr(y), _ptr(z), _ptr(weight), float(eps), groups,
+    _check(_launch("ssd_gated_rmsnorm", ctypes.byref(d), _ptr(y), _ptr(z), _ptr(weight), float(eps), groups,
                                             _ptr(out), s))
 
 
@@ -333,7 +371,7 @@ def ssd_total_decay(d, dt, A, total, stream=None):
     _expect_all([("dt", dt, sh["dt"], torch.float32), ("A", A, sh["A"], torch.float32),
                  ("total", total, (d.batch, d.nheads), torch.float32)])
     s = _stream(total.device) if stream is None else stream
-    _check(load_library().ssd_total_decay(ctypes.byref(d), _ptr(dt), _ptr(A), _ptr(total), s))
+    _check(_launch("ssd_total_decay", ctypes.byref(d), _ptr(dt), _ptr(A), _ptr(total), s))
 
 
 def ssd_fold_states(d, nshards, totals, shard_finals, initial_state, entering, stream=None):
@@ -343,55 +381,55 @@ def ssd_fold_states(d, nshards, totals, shard_finals, initial_state, entering, s
                  ("initial_state", initial_state, sh, torch.float32),
                  ("entering", entering, (nshards + 1,) + sh, torch.float32)])
     s = _stream(entering.device) if stream is None else stream
-    _check(load_library().ssd_fold_states(ctypes.byref(d), nshards, _ptr(totals), _ptr(shard_finals),
+    _check(_launch("ssd_fold_states", ctypes.byref(d), nshards, _ptr(totals), _ptr(shard_finals),
                                           _ptr(initial_state), _ptr(entering), s))
 
 
 def ssd_chunk_cumsum(d, dt, A, cs, stream=None):
     _check_io(d, dt=dt, A=A, cs=cs)
     s = _stream(dt.device) if stream is None else stream
-    _check(load_library().ssd_chunk_cumsum(ctypes.byref(d), _ptr(dt), _ptr(A), _ptr(cs), s))
+    _check(_launch("ssd_chunk_cumsum", ctypes.byref(d), _ptr(dt), _ptr(A), _ptr(cs), s))
 
 
 def ssd_chunk_state(d, x, dt, B, cs, states, stream=None):
     _check_io(d, x=x, dt=dt, B=B, cs=cs, states=states)
     s = _stream(x.device) if stream is None else stream
-    _check(load_library().ssd_chunk_state(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(B), _ptr(cs),
+    _check(_launch("ssd_chunk_state", ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(B), _ptr(cs),
                                           _ptr(states), s))
 
 
 def ssd_chunk_cumsum_state(d, x, dt, A, B, cs, states, stream=None):
     _check_io(d, x=x, dt=dt, A=A, B=B, cs=cs, states=states)
     s = _stream(x.device) if stream is None else stream
-    _check(load_library().ssd_chunk_cumsum_state(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
+    _check(_launch("ssd_chunk_cumsum_state", ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
                                                  _ptr(cs), _ptr(states), s))
 
 
 def ssd_state_passing(d, cs, states, final_state, stream=None):
     _check_io(d, cs=cs, states=states, final_state=final_state)
     s = _stream(final_state.device) if stream is None else stream
-    _check(load_library().ssd_state_passing(ctypes.byref(d), _ptr(cs), _ptr(states),
+    _check(_launch("ssd_state_passing", ctypes.byref(d), _ptr(cs), _ptr(states),
                                             _ptr(final_state), s))
 
 
 def ssd_state_passing_init(d, cs, states, initial_state, final_state, stream=None):
     _check_io(d, cs=cs, states=states, initial_state=initial_state, final_state=final_state)
     s = _stream(final_state.device) if stream is None else stream
-    _check(load_library().ssd_state_passing_init(ctypes.byref(d), _ptr(cs), _ptr(states),
+    _check(_launch("ssd_state_passing_init", ctypes.byref(d), _ptr(cs), _ptr(states),
                                                  _ptr(initial_state), _ptr(final_state), s))
 
 
 def ssd_chunk_scan_init(d, x, dt, B, C, D, cs, states, y, stream=None):
     _check_io(d, x=x, dt=dt, B=B, C=C, D=D, cs=cs, states=states, y=y)
     s = _stream(x.device) if stream is None else stream
-    _check(load_library().ssd_chunk_scan_init(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(B), _ptr(C),
+    _check(_launch("ssd_chunk_scan_init", ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(B), _ptr(C),
                                               _ptr(D), _ptr(cs), _ptr(states), _ptr(y), s))
 
 
 def ssd_chunk_scan(d, x, dt, B, C, D, cs, states, y, stream=None):
     _check_io(d, x=x, dt=dt, B=B, C=C, D=D, cs=cs, states=states, y=y)
     s = _stream(x.device) if stream is None else stream
-    _check(load_library().ssd_chunk_scan(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(B), _ptr(C),
+    _check(_launch("ssd_chunk_scan", ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(B), _ptr(C),
                                          _ptr(D), _ptr(cs), _ptr(states), _ptr(y), s))
 
 
@@ -403,7 +441,7 @@ def ssd_step(d, x, dt, A, B, C, D, state, y, stream=None):
                  ("C", C, (b, G, N), xt), ("D", D, (H,), torch.float32),
                  ("state", state, (b, H, N, P), torch.float32), ("y", y, (b, H, P), xt)])
     s = _stream(state.device) if stream is None else stream
-    _check(load_library().ssd_step(ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
+    _check(_launch("ssd_step", ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
                                    _ptr(D), _ptr(state), _ptr(y), s))
 
 

@@ -376,3 +376,19 @@ def test_noalloc_forward_argument_errors(lib):
     assert ssd.ssd_workspace_size(big) > ssd.ssd_noalloc_scratch_bytes()
     assert f(P(big), a, a, a, a, a, a, a, a, None) == 7
     assert f(P(dims(batch=0)), None, None, None, None, None, None, None, None, None) == OK
+
+
+def test_prepared_records_one_checked_call(lib):
+    """ssd.prepared runs a wrapper's checks once and records its C call
+    without making it; a function that makes no C call is refused."""
+    import torch
+    d = dims()
+    a = 0x500000
+    call = ssd.prepared(ssd.ssd_forward, d, a, a, a, a, a, a, a, a, a, 1 << 30, stream=0)
+    assert callable(call)
+    with pytest.raises(ValueError, match="made 0 C calls"):
+        ssd.prepared(lambda: None)
+    t = _inputs()
+    with pytest.raises(ValueError, match="must be on a CUDA device"):   # the checks still run
+        ssd.prepared(ssd.ssd_forward, ssd.dims_of(t["x"], t["B"], 32), t["x"], t["dt"], t["A"], t["B"], t["C"],
+                     t["D"], torch.empty_like(t["x"]), torch.zeros(2, 4, 16, 16), a, 1 << 30, stream=0)

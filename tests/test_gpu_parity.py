@@ -207,3 +207,21 @@ def test_forward_matches_stage_entry_points(T):
         torch.cuda.synchronize()
         assert torch.equal(y, out["y"]) and torch.equal(fin, out["final"])
         assert torch.equal(cs, out["cs"]) and torch.equal(S, out["S"])
+
+
+def test_prepared_call_matches_the_checked_call():
+    """A call repeated through ssd.prepared gives bitwise what the checked
+    wrapper gives."""
+    w = workload("m125", batch=2, seqlen=600, nheads=4)
+    g = to_dev(inputs.generate(w, seed=61))
+    d = ssd.dims_of(g["x"], g["B"], w.chunk_size, "bf16")
+    ws = ssd.alloc_workspace(d, "cuda")
+    y0, y1 = torch.empty_like(g["x"]), torch.full_like(g["x"], float("nan"))
+    f0 = torch.empty((w.batch, w.nheads, w.dstate, w.headdim), device="cuda")
+    f1 = torch.full_like(f0, float("nan"))
+    ssd.ssd_forward(d, g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], y0, f0, ws, ws.numel())
+    call = ssd.prepared(ssd.ssd_forward, d, g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], y1, f1, ws, ws.numel())
+    call()
+    call()
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1) and torch.equal(f0, f1)
