@@ -182,7 +182,11 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
             const float* csr = csbase + (int64_t)hh * hs * nc * Q;
             vcs = ldg(csr + min(i, Q - 1));
             vcr = ldg(csr + min(i | 31, Q - 1));
-            vdt = (i < qc) ? ldg(dtbase + hh * hs + (uint32_t)i * (uint32_t)H) : 0.0f;
+            // clamped row, zeroed past the chunk's end in store_vec: a select
+            // here would write the register before the load and make the
+            // wavefront wait for every older memory operation (the last
+            // head's stores) first
+            vdt = ldg(dtbase + hh * hs + (uint32_t)min(i, qc - 1) * (uint32_t)H);
         }
     };
     // per-head vectors in LDS, token i of the chunk's tiles (log2 units: c2 = cs log2 e):
@@ -193,9 +197,10 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
         const int i = threadIdx.x;
         if (i < QT) {
             const float c2 = vcs * kLog2e, c2r = vcr * kLog2e;
+            const float d = i < qc ? vdt : 0.0f;
             v[i] = c2;
-            v[QT + i] = exp2f(c2r - c2) * vdt;
-            v[2 * QT + i] = vdt;
+            v[QT + i] = exp2f(c2r - c2) * d;
+            v[2 * QT + i] = d;
         }
     };
 
@@ -333,12 +338,18 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
     if constexpr (VARLEN) sqj = active ? sqv[rt * 32 + l32] : 0;
 
     // ---- phase B: heads ----
-    // One head: start the copies of the next head's tiles into xn / hn (when
-    // double-buffered) and its vectors, compute this head from xt / ht / c2v,
-    // store y, and write the next head's vectors into vn. The LDS regions are passed as non-aliasing pointers so that the
-    // compiler knows this head's LDS reads do not depend on the copies in
-    // flight and does not wait for them (they are waited for explicitly at the
-    // end of the head). Returns false if some lane skipped a y store.
+    // One head: load the next head's vectors, compute this head from xt / ht /
+    // c2v, start the copies of the next head's tiles into xn / hn (when
+    // double-buffered), store y, and write the next head's vectors into vn.
+    // The copies are issued after the carried-state product, not at the start
+    // of the head: a wavefront stalls on issuing them while the memory system
+    // still holds the previous head's stores and the other wavefronts'
+    // copies, and at the start of the head that stall would delay its first
+    // products, which need nothing from memory. The LDS regions are passed as
+    // non-aliasing pointers so that the compiler knows this head's LDS reads
+    // do not depend on the copies in flight and does not wait for them (they
+    // are waited for explicitly at the end of the head). Returns false if
+    // some lane skipped a y store.
     // Operands of one 32-token key tile of the masked product, read from LDS
     // one step ahead of their use: the C B^T tile (off the diagonal), the
     // key tile's last c2, x fragments, and per-key vectors held one value per
@@ -357,11 +368,16 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
                     unsigned char* __restrict__ xn, unsigned char* __restrict__ hn,
                     float* __restrict__ vn, float Dh) __attribute__((always_inline)) {
         const bool more = hh + 1 < nh;
-        if (more) {
-            load_vec(hh + 1);   // before the copies: its results are waited for without them
-            if (NBX == 2) issue_x(hh + 1, xn);
-            if (NBH == 2 && hc) issue_h(hh + 1, hn);
-        }
+        // the next head's vectors first: their results are then waited for
+        // without the copies issued after them
+        if (more) load_vec(hh + 1);
+        auto issue_next = [&]() {
+            if (more) {
+                if (NBX == 2) issue_x(hh + 1, xn);
+                if (NBH == 2 && hc) issue_h(hh + 1, hn);
+            }
+        };
+        if (!active) issue_next();   // nothing to compute: issue at once
         bool stored_all = true;
         if (active) {
             const float* uv = c2v + QT;
@@ -517,6 +533,7 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
             } else {
                 load_stage(sa, 0);
             }
+            issue_next();
             // stages 0 .. rt (rt + 1 of them), two per iteration; the reads
             // past stage rt repeat stage rt's and go unused
             for (int k = 0; k <= rt; k += 2) {
