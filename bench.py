@@ -135,6 +135,69 @@ def attainable_peaks(torch, stream) -> dict | None:
                    "stream: 1 GiB read + 1 GiB write, 16-byte non-temporal vectors, 16384 workgroups; torch copy_: the same 1 GiB"}
 
 
+def scan_traffic(torch, stream, w, g, cs, states, scan_ms: float, scan_bytes: int) -> dict | None:
+    """The chunk scan's memory traffic with none of its arithmetic
+    (ssd_peak_scan_traffic in libssd_peak.so: same grid, heads per workgroup,
+    block order, copies and stores), timed with HIP events on the launch
+    stream: the time its own traffic pattern takes on this GPU, beside the
+    kernel's. bf16 inputs and states only."""
+    import ctypes
+
+    path = os.path.join(ROOT, "mamba_ssd_scan_04_amd", "libssd_peak.so")
+    if not os.path.exists(path) or w.dtype != "bf16" or states.dtype != torch.bfloat16:
+        return None
+    lib = ctypes.CDLL(path)
+    i64, vp = ctypes.c_int64, ctypes.c_void_p
+    lib.ssd_peak_scan_traffic.argtypes = [vp] * 8 + [i64] * 8 + [vp]
+    # heads per workgroup: the chunk scan's choice (whole rounds of one
+    # workgroup per compute unit, C B^T worth about 1.6 heads)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    chunks, hpg = w.batch * w.nchunks * w.ngroups, w.nheads // w.ngroups
+    hpw, best = 1, float("inf")
+    for h in range(1, min(hpg, 64) + 1):
+        nhb = -(-hpg // h)
+        cost = -(-chunks * nhb // cus) * (1.6 + -(-hpg // nhb))
+        if cost < best - 1e-9:
+            hpw, best = h, cost
+    nhb = -(-hpg // hpw)
+    y2 = torch.empty_like(g["x"])
+    sink = torch.empty(w.batch * w.nchunks * w.ngroups * nhb, dtype=torch.float32, device="cuda")
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+
+    def call():
+        rc = lib.ssd_peak_scan_traffic(ptr(g["x"]), ptr(g["B"]), ptr(g["C"]), ptr(states), ptr(g["dt"]), ptr(cs),
+                                       ptr(y2), ptr(sink), w.batch, w.seqlen, w.nheads, w.headdim, w.dstate,
+                                       w.ngroups, w.chunk_size, hpw, ctypes.c_void_p(stream.cuda_stream))
+        return rc
+
+    rc = call()
+    if rc == -1:
+        return None
+    if rc != 0:
+        raise RuntimeError(f"ssd_peak_scan_traffic failed ({rc})")
+    torch.cuda.synchronize()
+    if not torch.equal(y2, g["x"]):
+        raise RuntimeError("ssd_peak_scan_traffic: y != x")
+    for _ in range(5):
+        call()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 20
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del y2, sink
+    return {"ms": round(ms, 5), "GB/s": round(scan_bytes / (ms * 1e-3) / 1e9, 1),
+            "frac_of_peak": round(scan_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "chunk_scan_ms": round(scan_ms, 5), "chunk_scan_over_probe": round(scan_ms / ms, 4),
+            "heads_per_workgroup": hpw,
+            "how": "the chunk scan's copies, loads and stores at this shape with no arithmetic (libssd_peak.so "
+                   "ssd_peak_scan_traffic); GB/s counts the chunk scan's algorithmic bytes over the probe's time"}
+
+
 def source_sha(kernel: str) -> str:
     path = os.path.join(ROOT, "mamba_ssd_scan_04_amd", "csrc", SOURCES[kernel])
     h = hashlib.sha256()
@@ -647,6 +710,9 @@ def main() -> int:
         "design_bytes": dbytes, "design_us_at_peak": round(dbytes / (HBM_PEAK_GBS * 1e9) * 1e6, 2),
         "design_frac": round(dbytes / (HBM_PEAK_GBS * 1e9) / (ms_per_step * 1e-3), 4)}
     peaks = attainable_peaks(torch, stream)
+    if peaks is not None:
+        peaks["chunk_scan_traffic"] = scan_traffic(torch, stream, w, g, cs, states, kms["ssd_chunk_scan"],
+                                                   work["ssd_chunk_scan"]["bytes"])
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),

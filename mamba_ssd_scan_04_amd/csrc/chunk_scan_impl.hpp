@@ -553,6 +553,15 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
             // swap halves of quarters 2g and 2g+1 (v_permlane32_swap), so that
             // each lane holds 8 consecutive p (16 bytes) and a lane pair writes
             // 32 contiguous bytes of row j; fp32 stores 16 bytes per quarter.
+            // this token's x values for the D x term, all read before any is
+            // used (one wait instead of one per quarter pair)
+            typedef __attribute__((ext_vector_type(4))) T T4x;
+            T4x xq[PT][4];
+#pragma unroll
+            for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq)
+                    xq[pt][gq] = *reinterpret_cast<const T4x*>(xt + tile_byte<XRC>(jl, (pt * 32 + 8 * gq + 4 * hf) * ESZ));
             // the next head's vectors, before this head's stores: waiting for
             // their loads then needs only the copies issued after them
             if (more) store_vec(vn);
@@ -580,8 +589,7 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
 #pragma unroll
                         for (int q = 0; q < 2; ++q) {
                             const int gq = 2 * gp + q;
-                            const int xo = tile_byte<XRC>(jl, (pt * 32 + 8 * gq + 4 * hf) * ESZ);
-                            const bf16x4 xv = *reinterpret_cast<const bf16x4*>(xt + xo);
+                            const bf16x4 xv = xq[pt][gq];
                             u32x2 zp;
                             zp[0] = zw[q][0];
                             zp[1] = zw[q][1];
@@ -615,8 +623,7 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
 #pragma unroll
                     for (int gq = 0; gq < 4; ++gq) {
                         const int p0 = pt * 32 + 8 * gq + 4 * hf;
-                        const int xo = tile_byte<XRC>(jl, p0 * ESZ);
-                        const f32x4 xv = *reinterpret_cast<const f32x4*>(xt + xo);
+                        const f32x4 xv = xq[pt][gq];
                         f32x4 yv;
 #pragma unroll
                         for (int r = 0; r < 4; ++r) {

@@ -12,6 +12,16 @@
 //                        non-temporal loads in flight per thread, then their
 //                        stores: a plain read + write stream (bytes moved =
 //                        2 * 16 * n).
+//   ssd_peak_scan_traffic
+//                        the chunk scan's memory traffic with none of its
+//                        arithmetic: the same grid, workgroup size, heads per
+//                        workgroup and block order; per workgroup the chunk's
+//                        B and C rows, then per head the copies of the next
+//                        head's x tile and carried state into LDS (one head
+//                        ahead, double-buffered, as buffer loads straight to
+//                        LDS), its dt and cs values, and this head's y tile
+//                        stored from LDS (y = x, so the copy can be checked);
+//                        the copies are waited for and the stores are not.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -68,6 +78,132 @@ __global__ __launch_bounds__(256) void stream_kernel(const pk_u32x4* __restrict_
     for (; i < n; i += stride) y[i] = x[i];
 }
 
+struct ScanTraffic {
+    const unsigned char* x;
+    const unsigned char* B;
+    const unsigned char* C;
+    const unsigned char* states;
+    const float* dt;
+    const float* cs;
+    unsigned char* y;
+    float* sink;
+    int64_t T, H, P, N, G, Q, nc, hpw;
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t probe_rsrc(const void* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7FFFFFFF, 0x00020000);
+}
+
+// 16-byte pieces: piece k of a rows x rb tile (rb bytes per row) is row k / (rb/16),
+// bytes 16 (k % (rb/16)) of it; LDS holds the tile row-major, unswizzled.
+__device__ __forceinline__ void probe_copy_tile(unsigned char* lds, const unsigned char* g, int rows, int rb,
+                                                uint32_t stride) {
+    const __amdgpu_buffer_rsrc_t rs = probe_rsrc(g);
+    const int per_row = rb / 16, total = rows * per_row;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    for (int k0 = wave * 64; k0 < total; k0 += 512) {
+        const int k = k0 + lane;
+        const int kk = k < total ? k : total - 1;   // the last lanes of a partial group repeat a piece
+        const uint32_t off = (uint32_t)(kk / per_row) * stride + 16u * (uint32_t)(kk % per_row);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(lds + k0 * 16), 16, off,
+                                                 0, 0, 0);
+    }
+}
+
+__global__ __launch_bounds__(512) void scan_traffic_kernel(ScanTraffic a) {
+    extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+    const int64_t H = a.H, P = a.P, N = a.N, G = a.G, Q = a.Q, nc = a.nc;
+    const unsigned char* const xg = a.x;
+    const unsigned char* const sg = a.states;
+    const float* const csg = a.cs;
+    const float* const dtg = a.dt;
+    const int64_t hpg = H / G;
+    const int nhb = (int)((hpg + a.hpw - 1) / a.hpw);
+    const int total = (int)(gridDim.x * gridDim.y), id = (int)(blockIdx.x + gridDim.x * blockIdx.y);
+    const int lin = (total % 8 == 0) ? (id % 8) * (total / 8) + id / 8 : id;   // XCD-aware, as the chunk scan
+    int bx = lin % (int)gridDim.x;
+    const int hb = bx % nhb;
+    bx /= nhb;
+    const int64_t g = bx % G;
+    const int64_t c = bx / G;
+    const int64_t b = lin / (int)gridDim.x;
+    const int64_t h0 = g * hpg + hb;
+    const int nh = (int)((hpg - hb + nhb - 1) / nhb);
+    const int64_t tok0 = b * a.T + c * Q;
+    const int xrb = (int)(P * 2), hrb = (int)(P * N * 2);
+    const int XB = (int)(Q * xrb), HB = hrb;
+    const uint32_t xstride = (uint32_t)(H * P * 2);
+    float acc = 0.0f;
+    // the chunk's B and C rows (group g), read into registers, every load
+    // issued before any is used (at most 8 16-byte pieces of each per thread)
+    {
+        uint4 vb[8], vc[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int64_t k = threadIdx.x + 512 * u;
+            const int64_t kk = k < Q * N / 8 ? k : Q * N / 8 - 1;
+            const int64_t o = ((tok0 + kk / (N / 8)) * G + g) * N + 8 * (kk % (N / 8));
+            vb[u] = *reinterpret_cast<const uint4*>(a.B + 2 * o);
+            vc[u] = *reinterpret_cast<const uint4*>(a.C + 2 * o);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            acc += (float)(vb[u].x ^ vb[u].y ^ vb[u].z ^ vb[u].w ^ vc[u].x ^ vc[u].y ^ vc[u].z ^ vc[u].w);
+    }
+    // per head: the x tile, the carried state (none for chunk 0) and the
+    // head's Q cs and Q dt values (waves 0-3: cs, 4-7: dt, 4 bytes per lane)
+    unsigned char* const vl = smem + 2 * XB + 2 * HB;   // [2][2][256] floats
+    auto issue_into = [&](int hh, unsigned char* xl, unsigned char* hl, unsigned char* vb) __attribute__((always_inline)) {
+        const int64_t h = h0 + (int64_t)hh * nhb;
+        probe_copy_tile(xl, xg + (tok0 * H + h) * P * 2, (int)Q, xrb, xstride);
+        if (c > 0) probe_copy_tile(hl, sg + ((b * nc + c) * H + h) * P * N * 2, 1, hrb, 0);
+        const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+        const int i = (wave & 3) * 64 + lane, ic = i < Q ? i : (int)Q - 1;
+        unsigned char* dst = vb + (wave >> 2) * 1024 + (wave & 3) * 256;
+        const uint32_t off = wave < 4 ? 4u * (uint32_t)(((b * H + h) * nc + c) * Q + ic)
+                                      : 4u * (uint32_t)((tok0 + ic) * H + h);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(probe_rsrc(wave < 4 ? (const void*)csg : (const void*)dtg),
+                                                 (__attribute__((address_space(3))) void*)dst, 4, off, 0, 0, 0);
+    };
+    if (nh > 0) issue_into(0, smem, smem + 2 * XB, vl);
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+    unsigned char* const yb = a.y;
+    // one head: copies of the next head into the other buffers, y from this
+    // head's x tile; the buffers as non-aliasing pointers, so that the LDS
+    // reads of this head do not wait for the copies in flight
+    auto head = [&](int hh, const unsigned char* __restrict__ xl, unsigned char* __restrict__ xn,
+                    unsigned char* __restrict__ hn, unsigned char* __restrict__ vn) __attribute__((always_inline)) {
+        const int64_t h = h0 + (int64_t)hh * nhb;
+        if (hh + 1 < nh) issue_into(hh + 1, xn, hn, vn);
+        // y tile of this head = its x tile, 16 bytes per lane per store
+        unsigned char* yg = yb + (tok0 * H + h) * P * 2;
+        const int per_row = xrb / 16;
+        int nst = 0;
+        for (int k = threadIdx.x; k < Q * per_row; k += 512, ++nst) {
+            const uint4 v = *reinterpret_cast<const uint4*>(xl + 16 * k);
+            *reinterpret_cast<uint4*>(yg + (uint32_t)(k / per_row) * xstride + 16 * (k % per_row)) = v;
+        }
+        // the copies have landed: every memory operation of this wavefront
+        // but its nst stores (vmcnt(nst), gfx9 encoding) has completed
+        switch (nst) {
+            case 1: __builtin_amdgcn_s_waitcnt(0x0f71); break;
+            case 2: __builtin_amdgcn_s_waitcnt(0x0f72); break;
+            case 3: __builtin_amdgcn_s_waitcnt(0x0f73); break;
+            case 4: __builtin_amdgcn_s_waitcnt(0x0f74); break;
+            default: __builtin_amdgcn_s_waitcnt(0x0f70); break;
+        }
+        __builtin_amdgcn_s_barrier();
+    };
+    for (int hh = 0; hh < nh; ++hh) {
+        const int cur = hh & 1, nxt = cur ^ 1;
+        head(hh, smem + cur * XB, smem + nxt * XB, smem + 2 * XB + nxt * HB, vl + nxt * 2048);
+        acc += reinterpret_cast<const float*>(vl + nxt * 2048)[threadIdx.x & 255];
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    if (threadIdx.x == 0) a.sink[lin] = acc;
+}
+
 }  // namespace
 
 extern "C" {
@@ -88,6 +224,34 @@ int ssd_peak_stream(const void* x, void* y, int64_t n, int64_t blocks, hipStream
     if (((uintptr_t)x | (uintptr_t)y) & 15) return (int)hipErrorInvalidValue;
     hipLaunchKernelGGL(stream_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                        static_cast<const pk_u32x4*>(x), static_cast<pk_u32x4*>(y), n);
+    return (int)hipGetLastError();
+}
+
+// The chunk scan's traffic at one problem shape (bf16 x, B, C, states and y;
+// fp32 dt and cs; every dimension as the chunk scan takes it; T a multiple of
+// Q, Q <= 256, Q N <= 32768, whole 64-lane groups of 16-byte pieces in the x
+// tile (Q P / 512) and the state (P N / 512), 4 Q P + 4 P N + 4096 bytes of
+// LDS at most 160 KiB), with `hpw` heads per workgroup and `sink` holding one float per
+// workgroup. y receives x. Returns a hipError_t value, or -1 for a shape it
+// does not cover.
+int ssd_peak_scan_traffic(const void* x, const void* B, const void* C, const void* states, const float* dt,
+                          const float* cs, void* y, float* sink, int64_t batch, int64_t T, int64_t H, int64_t P,
+                          int64_t N, int64_t G, int64_t Q, int64_t hpw, hipStream_t stream) {
+    if (!x || !B || !C || !states || !dt || !cs || !y || !sink) return (int)hipErrorInvalidValue;
+    if (batch <= 0 || T <= 0 || Q <= 0 || Q > 256 || T % Q != 0 || G <= 0 || H % G != 0 || P % 8 != 0 ||
+        N % 8 != 0 || hpw <= 0)
+        return -1;
+    const int64_t lds = 2 * Q * P * 2 + 2 * P * N * 2 + 4096;
+    if (lds > 160 * 1024 || (Q * P * 2 / 16) % 64 != 0 || (P * N * 2 / 16) % 64 != 0 || Q * N > 32768) return -1;
+    ScanTraffic a{static_cast<const unsigned char*>(x), static_cast<const unsigned char*>(B),
+                  static_cast<const unsigned char*>(C), static_cast<const unsigned char*>(states), dt, cs,
+                  static_cast<unsigned char*>(y), sink, T, H, P, N, G, Q, T / Q, hpw};
+    const int64_t nhb = (H / G + hpw - 1) / hpw;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(scan_traffic_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e != hipSuccess) return (int)e;
+    hipLaunchKernelGGL(scan_traffic_kernel, dim3((unsigned)(a.nc * G * nhb), (unsigned)batch), dim3(512), (unsigned)lds,
+                       stream, a);
     return (int)hipGetLastError();
 }
 
