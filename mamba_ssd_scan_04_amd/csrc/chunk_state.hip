@@ -15,7 +15,8 @@
 // k-major operand.
 //
 // Work split. One workgroup (4 wavefronts) takes one chunk and up to HPW heads
-// of one group, which share B. The chunk is consumed in blocks of 32 tokens
+// of one group, which share B (fewer heads, more workgroups, when the grid
+// would not fill the chip). The chunk is consumed in blocks of 32 tokens
 // through a ring of NBUF LDS buffers: while the matrix cores work on block k,
 // buffer loads straight to LDS (no registers) fill blocks k+1 .. k+NBUF-1, and
 // the barrier between blocks does not drain them (lds_barrier). B and x blocks
@@ -34,10 +35,13 @@ namespace ssd {
 
 constexpr int kStateKB = 32;     // tokens per pipeline block
 
-template <typename T, int PT, int NT>
+// SPLIT: wavefronts per head doubled (half as many heads per workgroup,
+// twice as many workgroups) for grids that would not fill the chip.
+template <typename T, int PT, int NT, bool SPLIT = false>
 struct StateCfg {
     static constexpr int TILES = PT * NT;
-    static constexpr int WPH = TILES <= 8 ? 1 : TILES / 8;   // wavefronts per head
+    static constexpr int WPH0 = TILES <= 8 ? 1 : TILES / 8;
+    static constexpr int WPH = SPLIT ? 2 * WPH0 : WPH0;     // wavefronts per head
     static constexpr int HPW = 4 / WPH;                      // heads per workgroup
     static constexpr int PTW = PT / WPH;                     // p tiles per wavefront
     static constexpr int EPC = 16 / (int)sizeof(T);          // elements per 16-byte chunk
@@ -96,9 +100,9 @@ constexpr uint32_t kOob = 0x80000000u;   // buffer offset past every range: the 
 // ssd_chunk_cumsum; else read the given cs. VARLEN (with FUSED only): packed
 // documents, w_j = 0 for tokens outside the document of the chunk's last
 // token (the decay is 0 at a document start, "Transformers are SSMs", Knowl 8).
-template <typename T, int PT, int NT, typename ST, bool FUSED, bool VARLEN>
+template <typename T, int PT, int NT, typename ST, bool FUSED, bool VARLEN, bool SPLIT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void ssd_chunk_state_kernel(Params p) {
-    using Cfg = StateCfg<T, PT, NT>;
+    using Cfg = StateCfg<T, PT, NT, SPLIT>;
     using V8 = typename Vec8<T>::type;
     constexpr int HPW = Cfg::HPW, WPH = Cfg::WPH, PTW = Cfg::PTW;
     constexpr int ESZ = (int)sizeof(T);
@@ -376,20 +380,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
 }
 
-template <typename T, int PT, int NT, typename ST>
-static hipError_t launch_cs(const Params& p, hipStream_t s) {
-    using Cfg = StateCfg<T, PT, NT>;
+template <typename T, int PT, int NT, typename ST, bool SPLIT>
+static hipError_t launch_cs2(const Params& p, hipStream_t s) {
+    using Cfg = StateCfg<T, PT, NT, SPLIT>;
     const int64_t nhb = (p.heads_per_group + Cfg::HPW - 1) / Cfg::HPW;
     dim3 grid((unsigned)(p.nchunks * p.ngroups * nhb), (unsigned)p.batch);
     if (p.fuse_cs && p.seq_idx)
-        hipLaunchKernelGGL((ssd_chunk_state_kernel<T, PT, NT, ST, true, true>), grid, dim3(256), 0, s, p);
+        hipLaunchKernelGGL((ssd_chunk_state_kernel<T, PT, NT, ST, true, true, SPLIT>), grid, dim3(256), 0, s, p);
     else if (p.fuse_cs)
-        hipLaunchKernelGGL((ssd_chunk_state_kernel<T, PT, NT, ST, true, false>), grid, dim3(256), 0, s, p);
+        hipLaunchKernelGGL((ssd_chunk_state_kernel<T, PT, NT, ST, true, false, SPLIT>), grid, dim3(256), 0, s, p);
     else if (!p.seq_idx)
-        hipLaunchKernelGGL((ssd_chunk_state_kernel<T, PT, NT, ST, false, false>), grid, dim3(256), 0, s, p);
+        hipLaunchKernelGGL((ssd_chunk_state_kernel<T, PT, NT, ST, false, false, SPLIT>), grid, dim3(256), 0, s, p);
     else
         return hipErrorInvalidValue;   // document resets need the fused prefix sums
     return hipGetLastError();
+}
+
+// Two workgroups fit per compute unit: when the grid of whole head blocks
+// would not fill every such slot, halve the heads per workgroup (two
+// wavefronts per head) where the p tiles allow it.
+template <typename T, int PT, int NT, typename ST>
+static hipError_t launch_cs(const Params& p, hipStream_t s) {
+    using Cfg = StateCfg<T, PT, NT, false>;
+    if constexpr (PT >= 2 * Cfg::WPH0) {
+        const int64_t nhb = (p.heads_per_group + Cfg::HPW - 1) / Cfg::HPW;
+        if (p.batch * p.nchunks * p.ngroups * nhb < 2 * (int64_t)device_cus()) return launch_cs2<T, PT, NT, ST, true>(p, s);
+    }
+    return launch_cs2<T, PT, NT, ST, false>(p, s);
 }
 
 template <typename T, typename ST>
