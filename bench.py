@@ -572,6 +572,16 @@ def main() -> int:
         gated_norm()
     torch.cuda.synchronize()
     gated_norm_ms = (time.perf_counter() - tn) * 1e3 / args.steps
+    # the normalisation alone (in place, y read and written once)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        norm()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    norm_ms = e0.elapsed_time(e1) / args.steps
+    norm_bytes = 2 * yg.numel() * yg.element_size() + 4 * wn.numel()
     del zg, yg, wn
 
     # packed documents (ssd_forward_varlen): the same rows holding 8 documents
@@ -734,7 +744,11 @@ def main() -> int:
         "other_state_storage": alt,
         "gated": {"entry": "ssd_forward_gated", "ms_per_step": round(gated_ms, 5),
                   "tokens_per_s": round(w.batch * w.seqlen / (gated_ms * 1e-3), 1),
-                  "with_rmsnorm_ms_per_step": round(gated_norm_ms, 5)},
+                  "with_rmsnorm_ms_per_step": round(gated_norm_ms, 5),
+                  "rmsnorm_alone": {"kernel": "ssd_gated_rmsnorm", "ms": round(norm_ms, 5), "alg_bytes": norm_bytes,
+                                    "GB/s": round(norm_bytes / (norm_ms * 1e-3) / 1e9, 1),
+                                    "hbm_frac": round(norm_bytes / (norm_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                    "how": "in place on the gated output, event-timed on the launch stream"}},
         "varlen": {"entry": "ssd_forward_varlen", "documents_per_row": 8, "ms_per_step": round(varlen_ms, 5),
                    "tokens_per_s": round(w.batch * w.seqlen / (varlen_ms * 1e-3), 1)},
         "context_parallel": cp,

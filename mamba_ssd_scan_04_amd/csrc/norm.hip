@@ -9,11 +9,13 @@
 //
 //   g = y * silu(z)   (y itself without z),   out = g / sqrt(mean(g^2) + eps) * w
 //
-// One pass over HBM per tensor: a wavefront takes one (token, group), reads
-// its channels in 16-byte pieces (the sum of squares), reduces across lanes in
-// a fixed order, and reads them again (from cache) to scale and store. out
-// may be y itself: every element is read by the lane that writes it, before
-// it writes it.
+// One pass over HBM per tensor: a wavefront takes one (token, group) and its
+// channels in 16-byte pieces, lane l pieces l, l + 64, ... When a group has
+// at most MAXP pieces per lane the pieces are all loaded at once into
+// registers, the sum of squares reduced across lanes in a fixed order, and
+// the scaled values stored from the registers; larger groups read their
+// pieces twice (the second time from cache). out may be y itself: every
+// element is read by the lane that writes it, before it writes it.
 #include "kernels.hpp"
 
 namespace ssd {
@@ -48,6 +50,74 @@ template <> struct Pk8<float> {
 };
 
 constexpr int kNormWaves = 4;
+
+// y * silu(z) of one 16-byte piece (y alone without the gate), in fp32
+template <typename T, bool GATE>
+__device__ __forceinline__ void gate8(const typename Vec8<T>::type& ry, const typename Vec8<T>::type& rz, float (&v)[8]) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        v[k] = to_f32(ry[k]);
+        if constexpr (GATE) {
+            const float zk = to_f32(rz[k]);
+            v[k] = v[k] * (zk / (1.0f + expf(-zk)));
+        }
+    }
+}
+
+// Groups of at most 64 MAXP pieces: every piece read once, all of a lane's
+// loads issued before any is used.
+template <typename T, bool GATE, int MAXP>
+__global__ __launch_bounds__(64 * kNormWaves) void ssd_gated_rmsnorm_reg_kernel(const T* y, const T* __restrict__ z,
+                                                                                const float* __restrict__ w, float eps,
+                                                                                int64_t rows, int64_t groups,
+                                                                                int64_t cg, T* out) {
+    using V8 = typename Vec8<T>::type;
+    const int64_t item = (int64_t)blockIdx.x * kNormWaves + (threadIdx.x >> 6);
+    if (item >= rows) return;   // uniform per wavefront
+    const int lane = threadIdx.x & 63;
+    const int64_t base = item * cg;
+    const float* wg = w + (item % groups) * cg;
+    const int np = (int)((cg / 8 + 63) / 64);   // pieces per lane, at most MAXP
+    V8 ry[MAXP], rz[GATE ? MAXP : 1];
+#pragma unroll
+    for (int j = 0; j < MAXP; ++j) {
+        if (j < np) {
+            // lanes past the group's end load its last piece and add nothing
+            const int64_t c = min<int64_t>((int64_t)(lane + 64 * j) * 8, cg - 8);
+            ry[j] = ldg8(y + base + c);
+            if constexpr (GATE) rz[j] = ldg8(z + base + c);
+        }
+    }
+    float ss = 0.0f;
+#pragma unroll
+    for (int j = 0; j < MAXP; ++j) {
+        if (j < np && (int64_t)(lane + 64 * j) * 8 < cg) {
+            float v[8];
+            gate8<T, GATE>(ry[j], rz[GATE ? j : 0], v);
+#pragma unroll
+            for (int k = 0; k < 8; ++k) ss += v[k] * v[k];
+        }
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
+    const float r = 1.0f / sqrtf(ss / (float)cg + eps);
+#pragma unroll
+    for (int j = 0; j < MAXP; ++j) {
+        const int64_t c = (int64_t)(lane + 64 * j) * 8;
+        if (j < np && c < cg) {
+            float v[8];
+            gate8<T, GATE>(ry[j], rz[GATE ? j : 0], v);
+            const f32x4 w0 = *reinterpret_cast<const f32x4*>(wg + c);
+            const f32x4 w1 = *reinterpret_cast<const f32x4*>(wg + c + 4);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                v[k] = v[k] * r * w0[k];
+                v[4 + k] = v[4 + k] * r * w1[k];
+            }
+            Pk8<T>::store(out + base + c, v);
+        }
+    }
+}
 
 template <typename T, bool GATE>
 __global__ __launch_bounds__(64 * kNormWaves) void ssd_gated_rmsnorm_kernel(const T* y, const T* __restrict__ z,
@@ -96,6 +166,28 @@ template <typename T>
 static hipError_t launch_norm_t(const void* y, const void* z, const float* w, float eps, int64_t rows, int64_t groups,
                                 int64_t cg, void* out, hipStream_t s) {
     dim3 grid((unsigned)((rows + kNormWaves - 1) / kNormWaves));
+    // register-resident up to 16 (bf16) or 8 (fp32) pieces per lane, in the
+    // smallest instantiation that holds the group
+    const int64_t np = (cg / 8 + 63) / 64;
+#define SSD_NORM_REG(MAXP_)                                                                                       \
+    if (np <= MAXP_) {                                                                                            \
+        if (z)                                                                                                    \
+            hipLaunchKernelGGL((ssd_gated_rmsnorm_reg_kernel<T, true, MAXP_>), grid, dim3(64 * kNormWaves), 0, s, \
+                               static_cast<const T*>(y), static_cast<const T*>(z), w, eps, rows, groups, cg,      \
+                               static_cast<T*>(out));                                                             \
+        else                                                                                                      \
+            hipLaunchKernelGGL((ssd_gated_rmsnorm_reg_kernel<T, false, MAXP_>), grid, dim3(64 * kNormWaves), 0,  \
+                               s, static_cast<const T*>(y), static_cast<const T*>(nullptr), w, eps, rows, groups, \
+                               cg, static_cast<T*>(out));                                                         \
+        return hipGetLastError();                                                                                 \
+    }
+    SSD_NORM_REG(4)
+    SSD_NORM_REG(8)
+    if constexpr (sizeof(T) == 2) {
+        SSD_NORM_REG(12)
+        SSD_NORM_REG(16)
+    }
+#undef SSD_NORM_REG
     if (z)
         hipLaunchKernelGGL((ssd_gated_rmsnorm_kernel<T, true>), grid, dim3(64 * kNormWaves), 0, s,
                            static_cast<const T*>(y), static_cast<const T*>(z), w, eps, rows, groups, cg,
