@@ -211,16 +211,31 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
     // B is staged through LDS in slices of whole 32-token key tiles, in the
     // x buffer that head 0 does not use (or in head 0's, whose copy then
     // starts after phase A); if not even one key tile fits there, B tiles are
-    // read from global memory instead.
+    // read from global memory instead. With bf16 operands, two x buffers and
+    // C B^T in LDS, the whole of B is copied at once when the key tiles past
+    // the first slice fit in the C B^T region (whose tiles are then written
+    // only after every wavefront has read B): one round trip to memory, issued
+    // before head 0's copies, and waited for without them.
     constexpr int BRC = NT * 32 * ESZ / 16;                    // 16-byte chunks per B row
     constexpr int BTILE = 32 * BRC * 16;                       // one 32-token B tile
     unsigned char* const stg = smem + (NBX == 2 ? XB : 0);
     const int tps = XB / BTILE;                                // B tiles per slice
     const bool bstage = tps > 0;
-    if (nh > 0) {   // head 0's tiles start moving before phase A
-        load_vec(0);
-        if (NBX == 2 || !bstage) issue_x(0, smem);
-        if (hc) issue_h(0, hb0);
+    const bool bone = NBX == 2 && CBL && ESZ == 2 && bstage && (RT - tps) * BTILE <= Cfg::cbbytes(QT);
+    const unsigned char* const bbytes = reinterpret_cast<const unsigned char*>(bbase);
+    const uint32_t bstride = (uint32_t)(G * N * ESZ);
+    const int bvalid = (int)(N * ESZ / 16);
+    if (bone) {
+        // key tiles [0, tps) into the free x buffer, the rest into the C B^T
+        // region; rows past the chunk's last token re-read that token (their
+        // products get zero weight), a part wholly past it reads only it
+        const int r1 = min(RT, tps) * 32;
+        dma_tile<BRC>(stg, r1, qc, bvalid, bbytes, bstride, wave, kScanWaves, lane);
+        if (RT > tps) {
+            const int rb = min(r1, qc - 1);
+            dma_tile<BRC>(cbl0, RT * 32 - r1, qc - rb, bvalid, bbytes + (size_t)rb * bstride, bstride, wave,
+                          kScanWaves, lane);
+        }
     }
 
     const int nlast = (int)N - 8;
@@ -233,22 +248,32 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
     auto off = [&](int row, int ks) {
         return (uint32_t)min(row, qc - 1) * bcs + (uint32_t)min(ks * 16 + hf * 8, nlast);
     };
+    // this wave's C rows, zeroed past the chunk's end and past N where they
+    // are first used (a select here would wait for the loads at once)
     if (active) {
         const int jl = rt * 32 + l32;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const V8 raw = ldg8(cbase + off(jl, ks));
-            creg[ks] = (jl < qc && ks * 16 + hf * 8 < (int)N) ? raw : zero8<T>();
-        }
+        for (int ks = 0; ks < KS; ++ks) creg[ks] = ldg8(cbase + off(jl, ks));
+    }
+    auto mask_creg = [&]() {
+        const int jl = rt * 32 + l32;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) creg[ks] = (jl < qc && ks * 16 + hf * 8 < (int)N) ? creg[ks] : zero8<T>();
+    };
+    if (nh > 0) {   // head 0's tiles start moving before phase A
+        load_vec(0);
+        if (NBX == 2 || !bstage) issue_x(0, smem);
+        if (hc) issue_h(0, hb0);
     }
     // round tile kt of C B^T to the operand type and keep it
-    auto keep_tile = [&](int kt, const f32x16& acc) {
-        V8 lo, hi;
+    auto round_tile = [&](const f32x16& acc, V8& lo, V8& hi) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             lo[e] = from_f32<T>(acc[e]);
             hi[e] = from_f32<T>(acc[8 + e]);
         }
+    };
+    auto place_tile = [&](int kt, const V8& lo, const V8& hi) {
         if (kt < rt) {
             if constexpr (CBL) {
                 store8(reinterpret_cast<T*>(cbw + kt * Cfg::CBTILE) + lane * 8, lo);
@@ -262,10 +287,58 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
             cbd[1] = hi;
         }
     };
-    if (bstage) {
-        const unsigned char* bbytes = reinterpret_cast<const unsigned char*>(bbase);
-        const uint32_t bstride = (uint32_t)(G * N * ESZ);
-        const int bvalid = (int)(N * ESZ / 16);
+    auto keep_tile = [&](int kt, const f32x16& acc) {
+        V8 lo, hi;
+        round_tile(acc, lo, hi);
+        place_tile(kt, lo, hi);
+    };
+    if (bone) {
+        // B has landed when every memory operation of this wavefront but its
+        // head-0 tile copies has (its vector loads, older, are waited for too)
+        int younger = 0;
+        if (nh > 0) {
+#pragma unroll
+            for (int i = 0; i < NIX; ++i) younger += offx[i] >= 0 ? 1 : 0;
+            if (hc) {
+#pragma unroll
+                for (int i = 0; i < NIH; ++i) younger += offh[i] >= 0 ? 1 : 0;
+            }
+        }
+        wait_vmem_le_rt(younger);
+        lds_barrier();
+        // B's two parts as non-aliasing pointers, so that the compiler knows
+        // their reads do not depend on head 0's copies in flight
+        auto tiles = [&](const unsigned char* __restrict__ b1, const unsigned char* __restrict__ b2)
+            __attribute__((always_inline)) {
+            if (active) {
+                mask_creg();
+                V8 tlo[8], thi[8];
+#pragma unroll
+                for (int kt = 0; kt < 8; ++kt) {
+                    if (kt <= rt) {
+                        const T* tb = reinterpret_cast<const T*>(kt < tps ? b1 : b2);
+                        const int row = (kt < tps ? kt : kt - tps) * 32 + l32;
+                        f32x16 acc = zero16();
+#pragma unroll
+                        for (int ks = 0; ks < KS; ++ks) {
+                            V8 a = row8<BRC>(tb, row, ks * 16 + hf * 8);
+                            if (ks * 16 + hf * 8 >= (int)N) a = zero8<T>();
+                            mma_k16(acc, a, creg[ks]);
+                        }
+                        round_tile(acc, tlo[kt], thi[kt]);
+                    }
+                }
+                lds_barrier();   // every wavefront has read B from the C B^T region
+#pragma unroll
+                for (int kt = 0; kt < 8; ++kt)
+                    if (kt <= rt) place_tile(kt, tlo[kt], thi[kt]);
+            } else {
+                lds_barrier();
+            }
+        };
+        tiles(stg, cbl0);
+    } else if (bstage) {
+        if (active) mask_creg();
         for (int s0 = 0; s0 < RT; s0 += tps) {
             const int s1 = min(s0 + tps, RT);
             if (s0 > 0) lds_barrier();   // the previous slice has been read
@@ -295,6 +368,7 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
             issue_x(0, smem);
         }
     } else if (active) {
+        mask_creg();
         V8 bnext[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) bnext[ks] = ldg8(bbase + off(l32, ks));

@@ -225,6 +225,17 @@ def test_peak_probe_library_exports():
     assert peak.ssd_peak_mfma_bf16(4, 10, None, None) != 0
     assert peak.ssd_peak_stream(_fake(0x1000), _fake(0x2000), 0, 4, None) != 0
     assert peak.ssd_peak_stream(_fake(0x1008), _fake(0x2000), 16, 4, None) != 0
+    # the chunk scan's traffic probe: a null pointer, then shapes it does not
+    # cover (T not a multiple of Q, Q above 256, P not a multiple of 8, a tile
+    # that is not whole 64-lane groups), all rejected before any launch
+    i64, vp = ctypes.c_int64, ctypes.c_void_p
+    peak.ssd_peak_scan_traffic.argtypes = [vp] * 8 + [i64] * 8 + [vp]
+    ptrs = [_fake(0x10000 * (i + 1)) for i in range(8)]
+    assert peak.ssd_peak_scan_traffic(None, *ptrs[1:], 1, 512, 2, 64, 128, 1, 256, 1, None) != 0
+    assert peak.ssd_peak_scan_traffic(*ptrs, 1, 500, 2, 64, 128, 1, 256, 1, None) == -1
+    assert peak.ssd_peak_scan_traffic(*ptrs, 1, 1024, 2, 64, 128, 1, 512, 1, None) == -1
+    assert peak.ssd_peak_scan_traffic(*ptrs, 1, 512, 2, 60, 128, 1, 256, 1, None) == -1
+    assert peak.ssd_peak_scan_traffic(*ptrs, 1, 512, 2, 16, 16, 1, 32, 1, None) == -1
 
 
 def test_varlen_forward_argument_errors(lib):
