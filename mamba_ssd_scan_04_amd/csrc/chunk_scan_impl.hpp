@@ -214,8 +214,8 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
     // read from global memory instead. With bf16 operands, two x buffers and
     // C B^T in LDS, the whole of B is copied at once when the key tiles past
     // the first slice fit in the C B^T region (whose tiles are then written
-    // only after every wavefront has read B): one round trip to memory, issued
-    // before head 0's copies, and waited for without them.
+    // only after every wavefront has read B): one round trip to memory, in
+    // flight together with head 0's copies (issued after it).
     constexpr int BRC = NT * 32 * ESZ / 16;                    // 16-byte chunks per B row
     constexpr int BTILE = 32 * BRC * 16;                       // one 32-token B tile
     unsigned char* const stg = smem + (NBX == 2 ? XB : 0);
