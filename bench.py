@@ -135,6 +135,17 @@ def attainable_peaks(torch, stream) -> dict | None:
                    "stream: 1 GiB read + 1 GiB write, 16-byte non-temporal vectors, 16384 workgroups; torch copy_: the same 1 GiB"}
 
 
+def streams_x(w, state_esz: int) -> bool:
+    """The library's copy policy: x (and the chunk scan's carried states) are
+    copied non-temporally when the data of one forward (x, y, B, C, dt, cs and
+    the inter-chunk states) exceeds the 256 MiB last-level cache."""
+    esz = 2 if w.dtype == "bf16" else 4
+    bt = w.batch * w.seqlen
+    nbytes = (esz * bt * (2 * w.nheads * w.headdim + 2 * w.ngroups * w.dstate) + 8 * bt * w.nheads
+              + state_esz * w.batch * w.nchunks * w.nheads * w.headdim * w.dstate)
+    return nbytes > 256 * 2**20
+
+
 def scan_traffic(torch, stream, w, g, cs, states, scan_ms: float, scan_bytes: int) -> dict | None:
     """The chunk scan's memory traffic with none of its arithmetic
     (ssd_peak_scan_traffic in libssd_peak.so: same grid, heads per workgroup,
@@ -148,7 +159,8 @@ def scan_traffic(torch, stream, w, g, cs, states, scan_ms: float, scan_bytes: in
         return None
     lib = ctypes.CDLL(path)
     i64, vp = ctypes.c_int64, ctypes.c_void_p
-    lib.ssd_peak_scan_traffic.argtypes = [vp] * 8 + [i64] * 8 + [vp]
+    lib.ssd_peak_scan_traffic.argtypes = [vp] * 8 + [i64] * 9 + [vp]
+    nt = streams_x(w, 2)
     # heads per workgroup: the chunk scan's choice (whole rounds of one
     # workgroup per compute unit, C B^T worth about 1.6 heads)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
@@ -167,7 +179,7 @@ def scan_traffic(torch, stream, w, g, cs, states, scan_ms: float, scan_bytes: in
     def call():
         rc = lib.ssd_peak_scan_traffic(ptr(g["x"]), ptr(g["B"]), ptr(g["C"]), ptr(states), ptr(g["dt"]), ptr(cs),
                                        ptr(y2), ptr(sink), w.batch, w.seqlen, w.nheads, w.headdim, w.dstate,
-                                       w.ngroups, w.chunk_size, hpw, ctypes.c_void_p(stream.cuda_stream))
+                                       w.ngroups, w.chunk_size, hpw, int(nt), ctypes.c_void_p(stream.cuda_stream))
         return rc
 
     rc = call()
@@ -193,9 +205,75 @@ def scan_traffic(torch, stream, w, g, cs, states, scan_ms: float, scan_bytes: in
     return {"ms": round(ms, 5), "GB/s": round(scan_bytes / (ms * 1e-3) / 1e9, 1),
             "frac_of_peak": round(scan_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "chunk_scan_ms": round(scan_ms, 5), "chunk_scan_over_probe": round(scan_ms / ms, 4),
-            "heads_per_workgroup": hpw,
+            "heads_per_workgroup": hpw, "non_temporal_copies": nt,
             "how": "the chunk scan's copies, loads and stores at this shape with no arithmetic (libssd_peak.so "
                    "ssd_peak_scan_traffic); GB/s counts the chunk scan's algorithmic bytes over the probe's time"}
+
+
+def state_traffic(torch, stream, w, g, state_ms: float, state_bytes: int) -> dict | None:
+    """The chunk state's memory traffic with none of its arithmetic
+    (ssd_peak_state_traffic in libssd_peak.so: same grid, heads per workgroup,
+    block order, 3-deep copy ring, cs and state stores), timed with HIP events
+    on the launch stream, beside the kernel's time. bf16 inputs and states
+    only."""
+    import ctypes
+
+    path = os.path.join(ROOT, "mamba_ssd_scan_04_amd", "libssd_peak.so")
+    if not os.path.exists(path) or w.dtype != "bf16":
+        return None
+    lib = ctypes.CDLL(path)
+    i64, vp = ctypes.c_int64, ctypes.c_void_p
+    lib.ssd_peak_state_traffic.argtypes = [vp] * 5 + [i64] * 9 + [vp]
+    ntc = streams_x(w, 2)
+    # heads per workgroup: the chunk state's choice (4 wavefronts; one per head
+    # up to 8 output tiles of 32 x 32, halved when the grid would not fill
+    # both workgroup slots of every compute unit)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    pt, nt = -(-w.headdim // 32), -(-w.dstate // 32)
+    wph0 = 1 if pt * nt <= 8 else pt * nt // 8
+    hpg = w.nheads // w.ngroups
+    hpw = 4 // wph0
+    if pt >= 2 * wph0 and w.batch * w.nchunks * w.ngroups * -(-hpg // hpw) < 2 * cus:
+        hpw = 4 // (2 * wph0)
+    cs2 = torch.empty((w.batch, w.nheads, w.nchunks, w.chunk_size), dtype=torch.float32, device="cuda")
+    st2 = torch.empty((w.batch, w.nchunks, w.nheads, w.headdim, w.dstate), dtype=torch.bfloat16, device="cuda")
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())
+
+    def call():
+        return lib.ssd_peak_state_traffic(ptr(g["x"]), ptr(g["B"]), ptr(g["dt"]), ptr(cs2), ptr(st2), w.batch,
+                                          w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk_size, hpw,
+                                          int(ntc), ctypes.c_void_p(stream.cuda_stream))
+
+    rc = call()
+    if rc == -1:
+        return None
+    if rc != 0:
+        raise RuntimeError(f"ssd_peak_state_traffic failed ({rc})")
+    torch.cuda.synchronize()
+    x5 = g["x"].view(w.batch, w.nchunks, w.chunk_size, w.nheads, w.headdim)
+    last = x5[:, :, -32:].permute(0, 1, 3, 2, 4)          # [b][c][h][32][P]
+    want = last.unsqueeze(3).expand(-1, -1, -1, w.dstate // 32, -1, -1)
+    if not torch.equal(st2.view(want.shape), want) or not torch.equal(
+            cs2, g["dt"].view(w.batch, w.nchunks, w.chunk_size, w.nheads).permute(0, 3, 1, 2)):
+        raise RuntimeError("ssd_peak_state_traffic: wrong copy")
+    for _ in range(5):
+        call()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 20
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(reps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del cs2, st2
+    return {"ms": round(ms, 5), "GB/s": round(state_bytes / (ms * 1e-3) / 1e9, 1),
+            "frac_of_peak": round(state_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "chunk_state_ms": round(state_ms, 5), "chunk_state_over_probe": round(state_ms / ms, 4),
+            "heads_per_workgroup": hpw, "non_temporal_copies": ntc,
+            "how": "the chunk state's copies and stores at this shape with no arithmetic (libssd_peak.so "
+                   "ssd_peak_state_traffic); GB/s counts the chunk state's algorithmic bytes over the probe's time"}
 
 
 def source_sha(kernel: str) -> str:
@@ -723,6 +801,8 @@ def main() -> int:
     if peaks is not None:
         peaks["chunk_scan_traffic"] = scan_traffic(torch, stream, w, g, cs, states, kms["ssd_chunk_scan"],
                                                    work["ssd_chunk_scan"]["bytes"])
+        peaks["chunk_state_traffic"] = state_traffic(torch, stream, w, g, kms["ssd_chunk_state"],
+                                                     work["ssd_chunk_state"]["bytes"])
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),

@@ -158,11 +158,22 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
     int offx[NIX], offh[NIH];
     dma_tile_plan<XRC, NIX>(offx, QT, qc, xvalid, xstride, wave, kScanWaves, lane);
     dma_tile_plan<HRC, NIH>(offh, PT * 32, (int)P, hvalid, (uint32_t)(N * SSZ), wave, kScanWaves, lane);
+    // x and the carried states are read once: non-temporal copies when the
+    // forward's data cannot stay in the last-level cache
+    const bool snt = p.stream_x != 0;
     auto issue_x = [&](int hh, unsigned char* dst) {
-        dma_tile_issue<NIX>(dst, xbase + (int64_t)hh * hs * P * ESZ, offx, wave, kScanWaves);
+        const unsigned char* src = xbase + (int64_t)hh * hs * P * ESZ;
+        if (snt)
+            dma_tile_issue<NIX, true>(dst, src, offx, wave, kScanWaves);
+        else
+            dma_tile_issue<NIX>(dst, src, offx, wave, kScanWaves);
     };
     auto issue_h = [&](int hh, unsigned char* dst) {
-        dma_tile_issue<NIH>(dst, sbase + (int64_t)hh * hs * P * N * SSZ, offh, wave, kScanWaves);
+        const unsigned char* src = sbase + (int64_t)hh * hs * P * N * SSZ;
+        if (snt)
+            dma_tile_issue<NIH, true>(dst, src, offh, wave, kScanWaves);
+        else
+            dma_tile_issue<NIH>(dst, src, offh, wave, kScanWaves);
     };
     float vcs = 0.0f, vcr = 0.0f, vdt = 0.0f;   // thread i holds token i of the next head
     // packed documents: thread i < QT holds the id of token i (clamped to the

@@ -78,13 +78,16 @@ __device__ __forceinline__ void dma_plan(int (&off)[NI], int valid_chunks, uint3
         }
     }
 }
-template <int NI>
+// NT: the non-temporal policy (see dma16p).
+template <int NI, bool NT = false>
 __device__ __forceinline__ void dma_issue(unsigned char* lds, const unsigned char* gbase, const int (&off)[NI],
                                           int wave) {
     const __amdgpu_buffer_rsrc_t rs = raw_rsrc(gbase);
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-        if (off[i] >= 0) dma16(rs, (uint32_t)off[i], lds + (wave + 4 * i) * 1024);
+        if (off[i] >= 0)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(lds + (wave + 4 * i) * 1024),
+                                                     16, (uint32_t)off[i], 0, 0, NT ? 2 : 0);
     }
 }
 
@@ -100,7 +103,9 @@ constexpr uint32_t kOob = 0x80000000u;   // buffer offset past every range: the 
 // ssd_chunk_cumsum; else read the given cs. VARLEN (with FUSED only): packed
 // documents, w_j = 0 for tokens outside the document of the chunk's last
 // token (the decay is 0 at a document start, "Transformers are SSMs", Knowl 8).
-template <typename T, int PT, int NT, typename ST, bool FUSED, bool VARLEN, bool SPLIT>
+// XNT: x is copied with the non-temporal policy (the forward's data exceeds
+// the last-level cache, so x would not stay there for its second read).
+template <typename T, int PT, int NT, typename ST, bool FUSED, bool VARLEN, bool SPLIT, bool XNT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void ssd_chunk_state_kernel(Params p) {
     using Cfg = StateCfg<T, PT, NT, SPLIT>;
     using V8 = typename Vec8<T>::type;
@@ -159,8 +164,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         if (r0 + kStateKB <= qc) {          // full block: precomputed lane offsets
             dma_issue<Cfg::NDB>(base, bbase + (uint32_t)r0 * bstride, offb, wave);
             for (int hq = 0; hq < nh; ++hq)
-                dma_issue<Cfg::NDX>(base + Cfg::BBYTES + hq * Cfg::XBYTES,
-                                    xbase + (uint32_t)r0 * xstride + (int64_t)hq * P * ESZ, offx, wave);
+                dma_issue<Cfg::NDX, XNT>(base + Cfg::BBYTES + hq * Cfg::XBYTES,
+                                         xbase + (uint32_t)r0 * xstride + (int64_t)hq * P * ESZ, offx, wave);
         } else {
             // rows past the chunk's last token re-read that token (their weight
             // w is 0); a block wholly past it reads only that token
@@ -169,7 +174,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             dma_tile<Cfg::BRC>(base, kStateKB, vrows, bvalid, bbase + (uint32_t)rb * bstride, bstride, wave, 4, lane);
             for (int hq = 0; hq < nh; ++hq)
                 dma_tile<Cfg::XRC>(base + Cfg::BBYTES + hq * Cfg::XBYTES, kStateKB, vrows, xvalid,
-                                   xbase + (uint32_t)rb * xstride + (int64_t)hq * P * ESZ, xstride, wave, 4, lane);
+                                   xbase + (uint32_t)rb * xstride + (int64_t)hq * P * ESZ, xstride, wave, 4, lane,
+                                   XNT);
         }
     };
 
@@ -380,17 +386,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
 }
 
-template <typename T, int PT, int NT, typename ST, bool SPLIT>
+template <typename T, int PT, int NT, typename ST, bool SPLIT, bool XNT>
 static hipError_t launch_cs2(const Params& p, hipStream_t s) {
     using Cfg = StateCfg<T, PT, NT, SPLIT>;
     const int64_t nhb = (p.heads_per_group + Cfg::HPW - 1) / Cfg::HPW;
     dim3 grid((unsigned)(p.nchunks * p.ngroups * nhb), (unsigned)p.batch);
     if (p.fuse_cs && p.seq_idx)
-        hipLaunchKernelGGL((ssd_chunk_state_kernel<T, PT, NT, ST, true, true, SPLIT>), grid, dim3(256), 0, s, p);
+        hipLaunchKernelGGL((ssd_chunk_state_kernel<T, PT, NT, ST, true, true, SPLIT, XNT>), grid, dim3(256), 0, s, p);
     else if (p.fuse_cs)
-        hipLaunchKernelGGL((ssd_chunk_state_kernel<T, PT, NT, ST, true, false, SPLIT>), grid, dim3(256), 0, s, p);
+        hipLaunchKernelGGL((ssd_chunk_state_kernel<T, PT, NT, ST, true, false, SPLIT, XNT>), grid, dim3(256), 0, s, p);
     else if (!p.seq_idx)
-        hipLaunchKernelGGL((ssd_chunk_state_kernel<T, PT, NT, ST, false, false, SPLIT>), grid, dim3(256), 0, s, p);
+        hipLaunchKernelGGL((ssd_chunk_state_kernel<T, PT, NT, ST, false, false, SPLIT, XNT>), grid, dim3(256), 0, s, p);
     else
         return hipErrorInvalidValue;   // document resets need the fused prefix sums
     return hipGetLastError();
@@ -398,15 +404,17 @@ static hipError_t launch_cs2(const Params& p, hipStream_t s) {
 
 // Two workgroups fit per compute unit: when the grid of whole head blocks
 // would not fill every such slot, halve the heads per workgroup (two
-// wavefronts per head) where the p tiles allow it.
+// wavefronts per head) where the p tiles allow it. Such a small grid never
+// takes the non-temporal copies.
 template <typename T, int PT, int NT, typename ST>
 static hipError_t launch_cs(const Params& p, hipStream_t s) {
     using Cfg = StateCfg<T, PT, NT, false>;
     if constexpr (PT >= 2 * Cfg::WPH0) {
         const int64_t nhb = (p.heads_per_group + Cfg::HPW - 1) / Cfg::HPW;
-        if (p.batch * p.nchunks * p.ngroups * nhb < 2 * (int64_t)device_cus()) return launch_cs2<T, PT, NT, ST, true>(p, s);
+        if (p.batch * p.nchunks * p.ngroups * nhb < 2 * (int64_t)device_cus())
+            return launch_cs2<T, PT, NT, ST, true, false>(p, s);
     }
-    return launch_cs2<T, PT, NT, ST, false>(p, s);
+    return p.stream_x ? launch_cs2<T, PT, NT, ST, false, true>(p, s) : launch_cs2<T, PT, NT, ST, false, false>(p, s);
 }
 
 template <typename T, typename ST>

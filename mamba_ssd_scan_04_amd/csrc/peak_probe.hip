@@ -22,6 +22,17 @@
 //                        LDS), its dt and cs values, and this head's y tile
 //                        stored from LDS (y = x, so the copy can be checked);
 //                        the copies are waited for and the stores are not.
+//   ssd_peak_state_traffic
+//                        the chunk state's memory traffic with none of its
+//                        arithmetic: the same grid, heads per workgroup and
+//                        block order, 4 wavefronts; per workgroup the chunk's
+//                        B rows and its heads' x rows in blocks of 32 tokens
+//                        through a 3-deep LDS ring (buffer loads straight to
+//                        LDS, two blocks in flight), the heads' dt values into
+//                        a side tile with the first block, then per head its
+//                        Q cs values (= dt) and its P x N state, made of the
+//                        last block's x rows repeated (so the copy can be
+//                        checked).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -88,6 +99,7 @@ struct ScanTraffic {
     unsigned char* y;
     float* sink;
     int64_t T, H, P, N, G, Q, nc, hpw;
+    int nt;   // x and state copies non-temporal
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t probe_rsrc(const void* base) {
@@ -96,6 +108,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t probe_rsrc(const void* base) {
 
 // 16-byte pieces: piece k of a rows x rb tile (rb bytes per row) is row k / (rb/16),
 // bytes 16 (k % (rb/16)) of it; LDS holds the tile row-major, unswizzled.
+// NT: the non-temporal policy (aux bit 1), as the kernels take it for data
+// whose footprint exceeds the last-level cache.
+template <bool NT>
 __device__ __forceinline__ void probe_copy_tile(unsigned char* lds, const unsigned char* g, int rows, int rb,
                                                 uint32_t stride) {
     const __amdgpu_buffer_rsrc_t rs = probe_rsrc(g);
@@ -106,7 +121,7 @@ __device__ __forceinline__ void probe_copy_tile(unsigned char* lds, const unsign
         const int kk = k < total ? k : total - 1;   // the last lanes of a partial group repeat a piece
         const uint32_t off = (uint32_t)(kk / per_row) * stride + 16u * (uint32_t)(kk % per_row);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(lds + k0 * 16), 16, off,
-                                                 0, 0, 0);
+                                                 0, 0, NT ? 2 : 0);
     }
 }
 
@@ -155,8 +170,13 @@ __global__ __launch_bounds__(512) void scan_traffic_kernel(ScanTraffic a) {
     unsigned char* const vl = smem + 2 * XB + 2 * HB;   // [2][2][256] floats
     auto issue_into = [&](int hh, unsigned char* xl, unsigned char* hl, unsigned char* vb) __attribute__((always_inline)) {
         const int64_t h = h0 + (int64_t)hh * nhb;
-        probe_copy_tile(xl, xg + (tok0 * H + h) * P * 2, (int)Q, xrb, xstride);
-        if (c > 0) probe_copy_tile(hl, sg + ((b * nc + c) * H + h) * P * N * 2, 1, hrb, 0);
+        if (a.nt) {
+            probe_copy_tile<true>(xl, xg + (tok0 * H + h) * P * 2, (int)Q, xrb, xstride);
+            if (c > 0) probe_copy_tile<true>(hl, sg + ((b * nc + c) * H + h) * P * N * 2, 1, hrb, 0);
+        } else {
+            probe_copy_tile<false>(xl, xg + (tok0 * H + h) * P * 2, (int)Q, xrb, xstride);
+            if (c > 0) probe_copy_tile<false>(hl, sg + ((b * nc + c) * H + h) * P * N * 2, 1, hrb, 0);
+        }
         const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
         const int i = (wave & 3) * 64 + lane, ic = i < Q ? i : (int)Q - 1;
         unsigned char* dst = vb + (wave >> 2) * 1024 + (wave & 3) * 256;
@@ -204,6 +224,128 @@ __global__ __launch_bounds__(512) void scan_traffic_kernel(ScanTraffic a) {
     if (threadIdx.x == 0) a.sink[lin] = acc;
 }
 
+struct StateTraffic {
+    const unsigned char* x;
+    const unsigned char* B;
+    const float* dt;
+    float* cs;
+    unsigned char* states;
+    int64_t T, H, P, N, G, Q, nc, hpw;
+    int nt;   // x copies non-temporal
+};
+
+// Copies of a rows x rb tile (16-byte pieces, row-major in LDS) by 4
+// wavefronts; rows * rb / 16 is a multiple of 256, so every wavefront issues
+// rows * rb / 4096 instructions.
+template <bool NT>
+__device__ __forceinline__ void probe_copy_tile4(unsigned char* lds, const unsigned char* g, int rows, int rb,
+                                                 uint32_t stride, int wave, int lane) {
+    const __amdgpu_buffer_rsrc_t rs = probe_rsrc(g);
+    const int per_row = rb / 16, total = rows * per_row;
+    for (int k0 = wave * 64; k0 < total; k0 += 256) {
+        const int k = k0 + lane;
+        const uint32_t off = (uint32_t)(k / per_row) * stride + 16u * (uint32_t)(k % per_row);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(lds + k0 * 16), 16, off,
+                                                 0, 0, NT ? 2 : 0);
+    }
+}
+
+constexpr int kStBlk = 32;   // tokens per ring block
+
+// wait until at most n (0..8) of this wavefront's vector memory operations are
+// outstanding (vmcnt(n), gfx9 encoding); larger n waits for all
+__device__ __forceinline__ void probe_wait_le(int n) {
+    switch (n) {
+        case 1: __builtin_amdgcn_s_waitcnt(0x0f71); break;
+        case 2: __builtin_amdgcn_s_waitcnt(0x0f72); break;
+        case 3: __builtin_amdgcn_s_waitcnt(0x0f73); break;
+        case 4: __builtin_amdgcn_s_waitcnt(0x0f74); break;
+        case 5: __builtin_amdgcn_s_waitcnt(0x0f75); break;
+        case 6: __builtin_amdgcn_s_waitcnt(0x0f76); break;
+        case 7: __builtin_amdgcn_s_waitcnt(0x0f77); break;
+        case 8: __builtin_amdgcn_s_waitcnt(0x0f78); break;
+        default: __builtin_amdgcn_s_waitcnt(0x0f70); break;
+    }
+}
+
+__global__ __launch_bounds__(256) void state_traffic_kernel(StateTraffic a) {
+    extern __shared__ __attribute__((aligned(1024))) unsigned char smem[];
+    const int64_t H = a.H, P = a.P, N = a.N, G = a.G, Q = a.Q, nc = a.nc, hpw = a.hpw;
+    const int64_t hpg = H / G;
+    const int nhb = (int)((hpg + hpw - 1) / hpw);
+    const int total = (int)(gridDim.x * gridDim.y), id = (int)(blockIdx.x + gridDim.x * blockIdx.y);
+    const int lin = (total % 8 == 0) ? (id % 8) * (total / 8) + id / 8 : id;   // XCD-aware, as the chunk state
+    int bx = lin % (int)gridDim.x;
+    const int hb = bx % nhb;
+    bx /= nhb;
+    const int64_t g = bx % G;
+    const int64_t c = bx / G;
+    const int64_t b = lin / (int)gridDim.x;
+    const int64_t h0 = g * hpg + (int64_t)hb * hpw;
+    const int nh = (int)(hpg - (int64_t)hb * hpw < hpw ? hpg - (int64_t)hb * hpw : hpw);
+    const int64_t tok0 = b * a.T + c * Q;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int xrb = (int)(P * 2), brb = (int)(N * 2);
+    const int XB = kStBlk * xrb, BB = kStBlk * brb, BUF = BB + (int)hpw * XB;
+    const uint32_t xstride = (uint32_t)(H * P * 2), bstride = (uint32_t)(G * N * 2);
+    const unsigned char* const xg = a.x + (tok0 * H + h0) * P * 2;
+    const unsigned char* const bg = a.B + (tok0 * G + g) * N * 2;
+    float* const side = reinterpret_cast<float*>(smem + 3 * BUF);   // [hpw][Q] dt, hpw * 256 floats
+    const int nblk = (int)(Q / kStBlk);
+    // copies per wavefront per block (every wavefront issues the same number)
+    const int per_block = (int)(kStBlk * brb / 4096 + nh * (kStBlk * xrb / 4096));
+    auto issue = [&](int blk, unsigned char* base) __attribute__((always_inline)) {
+        const uint32_t r0 = (uint32_t)(blk * kStBlk);
+        probe_copy_tile4<false>(base, bg + r0 * bstride, kStBlk, brb, bstride, wave, lane);
+        if (a.nt) {
+            for (int hq = 0; hq < nh; ++hq)
+                probe_copy_tile4<true>(base + BB + hq * XB, xg + r0 * xstride + (int64_t)hq * P * 2, kStBlk, xrb,
+                                       xstride, wave, lane);
+        } else {
+            for (int hq = 0; hq < nh; ++hq)
+                probe_copy_tile4<false>(base + BB + hq * XB, xg + r0 * xstride + (int64_t)hq * P * 2, kStBlk, xrb,
+                                        xstride, wave, lane);
+        }
+    };
+    // the side tile: value i = (head i / Q, token i % Q), 4 bytes per lane
+    const int sround = (int)((hpw * Q + 255) / 256);
+    issue(0, smem);
+    {
+        const __amdgpu_buffer_rsrc_t rd = probe_rsrc(a.dt);
+        for (int i = 0; i < sround; ++i) {
+            const int fi = (wave + 4 * i) * 64 + lane, hq = fi / (int)Q, j = fi - hq * (int)Q;
+            const bool ok = hq < nh;
+            const uint32_t off = ok ? 4u * (uint32_t)((tok0 + j) * H + h0 + hq) : 0x80000000u;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (__attribute__((address_space(3))) void*)(side + fi), 4, off,
+                                                     0, 0, 0);
+        }
+    }
+    if (nblk > 1) issue(1, smem + BUF);
+    probe_wait_le(nblk > 1 ? per_block : 0);   // block 0 and the side tile landed
+    __builtin_amdgcn_s_barrier();
+    for (int blk = 0; blk < nblk; ++blk) {
+        if (blk + 2 < nblk) issue(blk + 2, smem + ((blk + 2) % 3) * BUF);
+        // block blk + 1 landed; block blk + 2 may still be in flight
+        probe_wait_le(blk + 2 < nblk ? per_block : 0);
+        __builtin_amdgcn_s_barrier();
+    }
+    // per head: cs (= its dt values) and the state, the last block's x rows of
+    // the head repeated N / 32 times; the wavefronts of a head split the rows
+    const int wph = (int)(4 / hpw), hh = wave / wph, part = wave % wph;
+    if (hh < nh) {
+        const int64_t h = h0 + hh;
+        if (part == 0) {
+            float* csr = a.cs + ((b * H + h) * nc + c) * Q;
+            for (int j = lane; j < Q; j += 64) csr[j] = side[hh * Q + j];
+        }
+        const unsigned char* xt = smem + ((nblk - 1) % 3) * BUF + BB + hh * XB;
+        unsigned char* sg = a.states + ((b * nc + c) * H + h) * P * N * 2;
+        const int pieces = (int)(P * N * 2 / 16), xp = XB / 16;
+        for (int k = part * 64 + lane; k < pieces; k += wph * 64)
+            *reinterpret_cast<uint4*>(sg + 16 * (int64_t)k) = *reinterpret_cast<const uint4*>(xt + 16 * (k % xp));
+    }
+}
+
 }  // namespace
 
 extern "C" {
@@ -232,11 +374,12 @@ int ssd_peak_stream(const void* x, void* y, int64_t n, int64_t blocks, hipStream
 // Q, Q <= 256, Q N <= 32768, whole 64-lane groups of 16-byte pieces in the x
 // tile (Q P / 512) and the state (P N / 512), 4 Q P + 4 P N + 4096 bytes of
 // LDS at most 160 KiB), with `hpw` heads per workgroup and `sink` holding one float per
-// workgroup. y receives x. Returns a hipError_t value, or -1 for a shape it
-// does not cover.
+// workgroup. nt != 0: the x and state copies take the non-temporal policy.
+// y receives x. Returns a hipError_t value, or -1 for a shape it does not
+// cover.
 int ssd_peak_scan_traffic(const void* x, const void* B, const void* C, const void* states, const float* dt,
                           const float* cs, void* y, float* sink, int64_t batch, int64_t T, int64_t H, int64_t P,
-                          int64_t N, int64_t G, int64_t Q, int64_t hpw, hipStream_t stream) {
+                          int64_t N, int64_t G, int64_t Q, int64_t hpw, int64_t nt, hipStream_t stream) {
     if (!x || !B || !C || !states || !dt || !cs || !y || !sink) return (int)hipErrorInvalidValue;
     if (batch <= 0 || T <= 0 || Q <= 0 || Q > 256 || T % Q != 0 || G <= 0 || H % G != 0 || P % 8 != 0 ||
         N % 8 != 0 || hpw <= 0)
@@ -245,13 +388,44 @@ int ssd_peak_scan_traffic(const void* x, const void* B, const void* C, const voi
     if (lds > 160 * 1024 || (Q * P * 2 / 16) % 64 != 0 || (P * N * 2 / 16) % 64 != 0 || Q * N > 32768) return -1;
     ScanTraffic a{static_cast<const unsigned char*>(x), static_cast<const unsigned char*>(B),
                   static_cast<const unsigned char*>(C), static_cast<const unsigned char*>(states), dt, cs,
-                  static_cast<unsigned char*>(y), sink, T, H, P, N, G, Q, T / Q, hpw};
+                  static_cast<unsigned char*>(y), sink, T, H, P, N, G, Q, T / Q, hpw, nt != 0};
     const int64_t nhb = (H / G + hpw - 1) / hpw;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(scan_traffic_kernel),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (e != hipSuccess) return (int)e;
     hipLaunchKernelGGL(scan_traffic_kernel, dim3((unsigned)(a.nc * G * nhb), (unsigned)batch), dim3(512), (unsigned)lds,
                        stream, a);
+    return (int)hipGetLastError();
+}
+
+// The chunk state's traffic at one problem shape (bf16 x, B and states; fp32
+// dt and cs; every dimension as the chunk state takes it; T a multiple of Q,
+// Q a multiple of 32 and at most 256, P and N multiples of 64, hpw 1, 2 or 4
+// heads per workgroup), as the chunk state's launch: (T/Q) G ceil(H/G/hpw) x
+// batch workgroups of 4 wavefronts. cs receives dt ([b][H][T/Q][Q] from
+// [b][T][H]); the state of (b, chunk, head), [P][N], receives the head's x
+// rows of the chunk's last 32 tokens ([32][P]) repeated N / 32 times. nt != 0:
+// the x copies take the non-temporal policy. Returns a hipError_t value, or
+// -1 for a shape it does not cover.
+int ssd_peak_state_traffic(const void* x, const void* B, const float* dt, float* cs, void* states, int64_t batch,
+                           int64_t T, int64_t H, int64_t P, int64_t N, int64_t G, int64_t Q, int64_t hpw, int64_t nt,
+                           hipStream_t stream) {
+    if (!x || !B || !dt || !cs || !states) return (int)hipErrorInvalidValue;
+    if (batch <= 0 || T <= 0 || Q <= 0 || Q > 256 || Q % 32 != 0 || T % Q != 0 || G <= 0 || H % G != 0 ||
+        P % 64 != 0 || N % 64 != 0 || !(hpw == 1 || hpw == 2 || hpw == 4))
+        return -1;
+    const int64_t per_block = 32 * N * 2 / 4096 + hpw * (32 * P * 2 / 4096);
+    // the side tile takes whole 256-value rounds of the dt copies: hpw * 1024 bytes
+    const int64_t lds = 3 * (32 * N * 2 + hpw * 32 * P * 2) + hpw * 1024;
+    if (lds > 160 * 1024 || per_block > 8) return -1;
+    StateTraffic a{static_cast<const unsigned char*>(x), static_cast<const unsigned char*>(B), dt, cs,
+                   static_cast<unsigned char*>(states), T, H, P, N, G, Q, T / Q, hpw, nt != 0};
+    const int64_t nhb = (H / G + hpw - 1) / hpw;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(state_traffic_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e != hipSuccess) return (int)e;
+    hipLaunchKernelGGL(state_traffic_kernel, dim3((unsigned)(a.nc * G * nhb), (unsigned)batch), dim3(256),
+                       (unsigned)lds, stream, a);
     return (int)hipGetLastError();
 }
 

@@ -52,8 +52,26 @@ size_t states_bytes_of(const ssd_dims* d) {
     return (size_t)d->batch * nchunks_of(d) * d->nheads * d->headdim * d->dstate * esz;
 }
 
+// The last-level cache of an MI355X (AMD Infinity Cache) holds 256 MiB. When
+// the data of one forward (x, y, B, C, dt, cs and the inter-chunk states)
+// exceeds it, x cannot stay cached between its two reads (chunk state, chunk
+// scan) anyway: the copies of x, and the chunk scan's copies of the carried
+// states, then take the non-temporal policy, which leaves the cache to the
+// states that the next launch reads. Below the cache's size, streaming would
+// give up the hits of data still cached from an earlier call.
+constexpr double kLastLevelCacheBytes = 256.0 * 1024 * 1024;
+
+bool stream_x_of(const ssd_dims* d) {
+    const double esz = d->dtype == SSD_BF16 ? 2.0 : 4.0;
+    const double bt = (double)d->batch * (double)d->seqlen;
+    const double bytes = esz * bt * (2.0 * d->nheads * d->headdim + 2.0 * d->ngroups * d->dstate) +
+                         8.0 * bt * d->nheads + (double)states_bytes_of(d);
+    return bytes > kLastLevelCacheBytes;
+}
+
 ssd::Params make_params(const ssd_dims* d) {
     ssd::Params p{};
+    p.stream_x = stream_x_of(d) ? 1 : 0;
     p.batch = d->batch;
     p.seqlen = d->seqlen;
     p.nheads = d->nheads;

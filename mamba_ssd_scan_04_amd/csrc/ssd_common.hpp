@@ -47,6 +47,9 @@ struct Params {
     const void* z;             // gate input [b,T,H,P] (x's type): y *= silu(z); nullptr: no gate
     const int* seq_idx;        // document ids [b,T], non-decreasing along T: the state is reset where
                                // the id changes; nullptr: one sequence per batch row
+    int stream_x;              // copy x (chunk state, chunk scan) and the carried states (chunk
+                               // scan) to LDS with the non-temporal policy: set when the data of a
+                               // forward cannot stay in the last-level cache
 };
 
 // ---- element traits --------------------------------------------------------
@@ -207,6 +210,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base) {
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, unsigned char* lds) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
 }
+// The same copy with the cache policy picked at run time (nt uniform across
+// the wavefront): nt = non-temporal (the line is not kept in the caches on
+// the way), for data read once whose footprint exceeds the caches.
+__device__ __forceinline__ void dma16p(__amdgpu_buffer_rsrc_t rs, uint32_t voff, unsigned char* lds, bool nt) {
+    if (nt)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 2);
+    else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+}
 
 // Asynchronous global -> LDS copy of a rows x RC-chunk tile. Every lane of a
 // wavefront copies one 16-byte chunk per instruction; instruction k of the
@@ -219,7 +231,7 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, uint32_t voff, 
 template <int RC>
 __device__ __forceinline__ void dma_tile(unsigned char* lds, int rows, int valid_rows, int valid_chunks,
                                          const unsigned char* gbase, uint32_t row_stride, int wave,
-                                         int nwaves, int lane) {
+                                         int nwaves, int lane, bool nt = false) {
     const __amdgpu_buffer_rsrc_t rs = raw_rsrc(gbase);
     const int total = rows * RC;   // a multiple of 64
     for (int k = wave; k * 64 < total; k += nwaves) {
@@ -228,7 +240,7 @@ __device__ __forceinline__ void dma_tile(unsigned char* lds, int rows, int valid
         int c = (P % RC) ^ swz<RC>(r);
         c = c < valid_chunks ? c : valid_chunks - 1;
         const int rr = r < valid_rows ? r : valid_rows - 1;
-        dma16(rs, (uint32_t)rr * row_stride + 16u * (uint32_t)c, lds + k * 1024);
+        dma16p(rs, (uint32_t)rr * row_stride + 16u * (uint32_t)c, lds + k * 1024, nt);
     }
 }
 
@@ -253,13 +265,16 @@ __device__ __forceinline__ void dma_tile_plan(int (&off)[NI], int rows, int vali
         }
     }
 }
-template <int NI>
+// NT: the non-temporal policy (see dma16p).
+template <int NI, bool NT = false>
 __device__ __forceinline__ void dma_tile_issue(unsigned char* lds, const unsigned char* gbase, const int (&off)[NI],
                                                int wave, int nwaves) {
     const __amdgpu_buffer_rsrc_t rs = raw_rsrc(gbase);
 #pragma unroll
     for (int i = 0; i < NI; ++i)
-        if (off[i] >= 0) dma16(rs, (uint32_t)off[i], lds + (wave + nwaves * i) * 1024);
+        if (off[i] >= 0)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(lds + (wave + nwaves * i) * 1024),
+                                                     16, (uint32_t)off[i], 0, 0, NT ? 2 : 0);
 }
 
 // Loads through explicit global-address-space pointers (not flat).

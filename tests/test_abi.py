@@ -229,13 +229,23 @@ def test_peak_probe_library_exports():
     # cover (T not a multiple of Q, Q above 256, P not a multiple of 8, a tile
     # that is not whole 64-lane groups), all rejected before any launch
     i64, vp = ctypes.c_int64, ctypes.c_void_p
-    peak.ssd_peak_scan_traffic.argtypes = [vp] * 8 + [i64] * 8 + [vp]
+    peak.ssd_peak_scan_traffic.argtypes = [vp] * 8 + [i64] * 9 + [vp]
     ptrs = [_fake(0x10000 * (i + 1)) for i in range(8)]
-    assert peak.ssd_peak_scan_traffic(None, *ptrs[1:], 1, 512, 2, 64, 128, 1, 256, 1, None) != 0
-    assert peak.ssd_peak_scan_traffic(*ptrs, 1, 500, 2, 64, 128, 1, 256, 1, None) == -1
-    assert peak.ssd_peak_scan_traffic(*ptrs, 1, 1024, 2, 64, 128, 1, 512, 1, None) == -1
-    assert peak.ssd_peak_scan_traffic(*ptrs, 1, 512, 2, 60, 128, 1, 256, 1, None) == -1
-    assert peak.ssd_peak_scan_traffic(*ptrs, 1, 512, 2, 16, 16, 1, 32, 1, None) == -1
+    assert peak.ssd_peak_scan_traffic(None, *ptrs[1:], 1, 512, 2, 64, 128, 1, 256, 1, 0, None) != 0
+    assert peak.ssd_peak_scan_traffic(*ptrs, 1, 500, 2, 64, 128, 1, 256, 1, 0, None) == -1
+    assert peak.ssd_peak_scan_traffic(*ptrs, 1, 1024, 2, 64, 128, 1, 512, 1, 0, None) == -1
+    assert peak.ssd_peak_scan_traffic(*ptrs, 1, 512, 2, 60, 128, 1, 256, 1, 0, None) == -1
+    assert peak.ssd_peak_scan_traffic(*ptrs, 1, 512, 2, 16, 16, 1, 32, 1, 0, None) == -1
+    # the chunk state's traffic probe: a null pointer, then shapes it does not
+    # cover (T not a multiple of Q, Q not a multiple of 32, P or N not a
+    # multiple of 64, 3 heads per workgroup)
+    peak.ssd_peak_state_traffic.argtypes = [vp] * 5 + [i64] * 9 + [vp]
+    assert peak.ssd_peak_state_traffic(None, *ptrs[1:5], 1, 512, 4, 64, 128, 1, 256, 4, 0, None) != 0
+    assert peak.ssd_peak_state_traffic(*ptrs[:5], 1, 500, 4, 64, 128, 1, 256, 4, 0, None) == -1
+    assert peak.ssd_peak_state_traffic(*ptrs[:5], 1, 512, 4, 64, 128, 1, 16, 4, 0, None) == -1
+    assert peak.ssd_peak_state_traffic(*ptrs[:5], 1, 512, 4, 32, 128, 1, 256, 4, 0, None) == -1
+    assert peak.ssd_peak_state_traffic(*ptrs[:5], 1, 512, 4, 64, 16, 1, 256, 4, 0, None) == -1
+    assert peak.ssd_peak_state_traffic(*ptrs[:5], 1, 512, 6, 64, 128, 1, 256, 3, 0, None) == -1
 
 
 def test_varlen_forward_argument_errors(lib):

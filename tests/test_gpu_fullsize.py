@@ -48,3 +48,41 @@ def test_fullsize_whole_output(name):
         record_parity("forward", name, sd, errs[sd][0].value(), errs[sd][1].value(), tol)
     for sd in storages:
         assert errs[sd][0].value() <= tol and errs[sd][1].value() <= tol, sd
+
+
+def test_streaming_copies_ragged_whole_output():
+    """A forward whose data exceeds the 256 MiB last-level cache takes the
+    non-temporal copies of x and the carried states; here with a ragged last
+    chunk (77 of 256 tokens), so the partial-block copies take that policy
+    too. Whole output against the oracle, both state storage types."""
+    w = inputs.WORKLOADS["m2p7"].replace(name="stream_ragged", batch=3, seqlen=32 * 256 + 77)
+    esz = 2
+    bt = w.batch * w.seqlen
+    footprint = (esz * bt * (2 * w.nheads * w.headdim + 2 * w.ngroups * w.dstate) + 8 * bt * w.nheads
+                 + esz * w.batch * w.nchunks * w.nheads * w.headdim * w.dstate)
+    assert footprint > 256 * 2**20
+    say(f"fullsize streaming ragged {w.describe()} footprint {footprint / 2**20:.0f} MiB")
+    inp = inputs.generate(w, seed=3)
+    dev = to_dev(inp)
+    outs = {}
+    for sd in ("fp32", "bf16"):
+        d = ssd.dims_of(dev["x"], dev["B"], w.chunk_size, sd)
+        ws = ssd.alloc_workspace(d, "cuda")
+        y = torch.empty_like(dev["x"])
+        fin = torch.empty((w.batch, w.nheads, w.dstate, w.headdim), dtype=torch.float32, device="cuda")
+        ssd.ssd_forward(d, dev["x"], dev["dt"], dev["A"], dev["B"], dev["C"], dev["D"], y, fin, ws, ws.numel())
+        torch.cuda.synchronize()
+        del ws
+        assert torch.isfinite(y.float()).all() and torch.isfinite(fin).all()
+        outs[sd] = (y, fin)
+    errs = {sd: (MaxRelErr(), MaxRelErr()) for sd in outs}
+    for b in range(w.batch):
+        y_ref, fin_ref = oracle_batch(inp, b)
+        for sd, (y, fin) in outs.items():
+            errs[sd][0].add(y[b].float().cpu().numpy(), y_ref[0])
+            errs[sd][1].add(fin[b].cpu().numpy(), fin_ref[0])
+    tol = TOL[w.dtype]
+    for sd in outs:
+        record_parity("forward", w.name, sd, errs[sd][0].value(), errs[sd][1].value(), tol)
+    for sd in outs:
+        assert errs[sd][0].value() <= tol and errs[sd][1].value() <= tol, sd
