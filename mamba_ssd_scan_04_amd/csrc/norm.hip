@@ -51,6 +51,22 @@ template <> struct Pk8<float> {
 
 constexpr int kNormWaves = 4;
 
+// A global load / store of one vector, NT: with the non-temporal policy (the
+// line is not kept in the caches), for passes whose data exceeds the
+// last-level cache.
+template <bool NT, typename V>
+__device__ __forceinline__ V gload(const V* p) {
+    const __attribute__((address_space(1))) V* q = (const __attribute__((address_space(1))) V*)p;
+    if constexpr (NT) return __builtin_nontemporal_load(q);
+    else return *q;
+}
+template <bool NT, typename V>
+__device__ __forceinline__ void gstore(V* p, const V& v) {
+    __attribute__((address_space(1))) V* q = (__attribute__((address_space(1))) V*)p;
+    if constexpr (NT) __builtin_nontemporal_store(v, q);
+    else *q = v;
+}
+
 // y * silu(z) of one 16-byte piece (y alone without the gate), in fp32
 template <typename T, bool GATE>
 __device__ __forceinline__ void gate8(const typename Vec8<T>::type& ry, const typename Vec8<T>::type& rz, float (&v)[8]) {
@@ -65,8 +81,9 @@ __device__ __forceinline__ void gate8(const typename Vec8<T>::type& ry, const ty
 }
 
 // Groups of at most 64 MAXP pieces: every piece read once, all of a lane's
-// loads issued before any is used.
-template <typename T, bool GATE, int MAXP>
+// loads issued before any is used. NT: y, z and out with the non-temporal
+// policy.
+template <typename T, bool GATE, int MAXP, bool NT>
 __global__ __launch_bounds__(64 * kNormWaves) void ssd_gated_rmsnorm_reg_kernel(const T* y, const T* __restrict__ z,
                                                                                 const float* __restrict__ w, float eps,
                                                                                 int64_t rows, int64_t groups,
@@ -84,8 +101,8 @@ __global__ __launch_bounds__(64 * kNormWaves) void ssd_gated_rmsnorm_reg_kernel(
         if (j < np) {
             // lanes past the group's end load its last piece and add nothing
             const int64_t c = min<int64_t>((int64_t)(lane + 64 * j) * 8, cg - 8);
-            ry[j] = ldg8(y + base + c);
-            if constexpr (GATE) rz[j] = ldg8(z + base + c);
+            ry[j] = gload<NT>(reinterpret_cast<const V8*>(y + base + c));
+            if constexpr (GATE) rz[j] = gload<NT>(reinterpret_cast<const V8*>(z + base + c));
         }
     }
     float ss = 0.0f;
@@ -114,7 +131,10 @@ __global__ __launch_bounds__(64 * kNormWaves) void ssd_gated_rmsnorm_reg_kernel(
                 v[k] = v[k] * r * w0[k];
                 v[4 + k] = v[4 + k] * r * w1[k];
             }
-            Pk8<T>::store(out + base + c, v);
+            V8 o;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) o[k] = from_f32<T>(v[k]);
+            gstore<NT>(reinterpret_cast<V8*>(out + base + c), o);
         }
     }
 }
@@ -162,6 +182,23 @@ __global__ __launch_bounds__(64 * kNormWaves) void ssd_gated_rmsnorm_kernel(cons
     }
 }
 
+template <typename T, int MAXP, bool NT>
+static void launch_norm_reg(dim3 grid, const void* y, const void* z, const float* w, float eps, int64_t rows,
+                            int64_t groups, int64_t cg, void* out, hipStream_t s) {
+    if (z)
+        hipLaunchKernelGGL((ssd_gated_rmsnorm_reg_kernel<T, true, MAXP, NT>), grid, dim3(64 * kNormWaves), 0, s,
+                           static_cast<const T*>(y), static_cast<const T*>(z), w, eps, rows, groups, cg,
+                           static_cast<T*>(out));
+    else
+        hipLaunchKernelGGL((ssd_gated_rmsnorm_reg_kernel<T, false, MAXP, NT>), grid, dim3(64 * kNormWaves), 0, s,
+                           static_cast<const T*>(y), static_cast<const T*>(nullptr), w, eps, rows, groups, cg,
+                           static_cast<T*>(out));
+}
+
+// The last-level cache of an MI355X (AMD Infinity Cache) holds 256 MiB: a
+// pass over more data than that streams it with the non-temporal policy.
+constexpr double kNormCacheBytes = 256.0 * 1024 * 1024;
+
 template <typename T>
 static hipError_t launch_norm_t(const void* y, const void* z, const float* w, float eps, int64_t rows, int64_t groups,
                                 int64_t cg, void* out, hipStream_t s) {
@@ -169,17 +206,14 @@ static hipError_t launch_norm_t(const void* y, const void* z, const float* w, fl
     // register-resident up to 16 (bf16) or 8 (fp32) pieces per lane, in the
     // smallest instantiation that holds the group
     const int64_t np = (cg / 8 + 63) / 64;
-#define SSD_NORM_REG(MAXP_)                                                                                       \
-    if (np <= MAXP_) {                                                                                            \
-        if (z)                                                                                                    \
-            hipLaunchKernelGGL((ssd_gated_rmsnorm_reg_kernel<T, true, MAXP_>), grid, dim3(64 * kNormWaves), 0, s, \
-                               static_cast<const T*>(y), static_cast<const T*>(z), w, eps, rows, groups, cg,      \
-                               static_cast<T*>(out));                                                             \
-        else                                                                                                      \
-            hipLaunchKernelGGL((ssd_gated_rmsnorm_reg_kernel<T, false, MAXP_>), grid, dim3(64 * kNormWaves), 0,  \
-                               s, static_cast<const T*>(y), static_cast<const T*>(nullptr), w, eps, rows, groups, \
-                               cg, static_cast<T*>(out));                                                         \
-        return hipGetLastError();                                                                                 \
+    const bool nt = (double)(z ? 3 : 2) * (double)rows * (double)cg * (double)sizeof(T) > kNormCacheBytes;
+#define SSD_NORM_REG(MAXP_)                                                                      \
+    if (np <= MAXP_) {                                                                           \
+        if (nt)                                                                                  \
+            launch_norm_reg<T, MAXP_, true>(grid, y, z, w, eps, rows, groups, cg, out, s);       \
+        else                                                                                     \
+            launch_norm_reg<T, MAXP_, false>(grid, y, z, w, eps, rows, groups, cg, out, s);      \
+        return hipGetLastError();                                                                \
     }
     SSD_NORM_REG(4)
     SSD_NORM_REG(8)

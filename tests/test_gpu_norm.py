@@ -87,3 +87,29 @@ def test_norm_full_size_layer_shape():
         e.add(_f64(out[b:b + 1]), ref)
     record_parity("rmsnorm", "m2p7", "bf16", e.value(), None, TOL[w.dtype])
     assert e.value() <= TOL[w.dtype]
+
+
+def test_norm_streaming_gate_in_place():
+    """A pass over more than the 256 MiB last-level cache (y, z and out of
+    b=3, T=4096, 80 heads of 64, bf16: 377 MB) takes the non-temporal loads
+    and stores: gated, in place and out of place, against the oracle over
+    every token."""
+    g = torch.Generator().manual_seed(78)
+    shape = (3, 4096, 80, 64)
+    y = torch.randn(shape, generator=g).to(torch.bfloat16)
+    z = torch.randn(shape, generator=g).to(torch.bfloat16)
+    wt = torch.randn(80 * 64, generator=g)
+    assert 3 * y.numel() * 2 > 256 * 2**20
+    say(f"norm streaming shape={shape} gate=True")
+    yd, zd, wd = y.cuda(), z.cuda(), wt.cuda()
+    out = ssd.gated_rmsnorm(yd, zd, wd, 1e-5, 1)
+    ssd.gated_rmsnorm(yd, zd, wd, 1e-5, 1, out=yd)
+    torch.cuda.synchronize()
+    assert torch.equal(out, yd)
+    e = MaxRelErr()
+    wn = wt.numpy()
+    for b in range(shape[0]):
+        ref = oracle.gated_rmsnorm(_f64(y[b:b + 1]), _f64(z[b:b + 1]), wn, 1e-5, 1)
+        e.add(_f64(out[b:b + 1]), ref)
+    say(f"  err={e.value():.3e}")
+    assert e.value() <= TOL["bf16"]
