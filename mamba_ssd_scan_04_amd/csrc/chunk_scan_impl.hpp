@@ -232,10 +232,25 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
     unsigned char* const stg = smem + (NBX == 2 ? XB : 0);
     const int tps = XB / BTILE;                                // B tiles per slice
     const bool bstage = tps > 0;
-    const bool bone = NBX == 2 && CBL && ESZ == 2 && bstage && (RT - tps) * BTILE <= Cfg::cbbytes(QT);
+    // (never with N > 128: the key tiles past the first slice are then larger
+    // than the C B^T region at every chunk size)
+    constexpr bool BONE_OK = NBX == 2 && CBL && ESZ == 2 && NT <= 4;
+    const bool bone = BONE_OK && bstage && (RT - tps) * BTILE <= Cfg::cbbytes(QT);
     const unsigned char* const bbytes = reinterpret_cast<const unsigned char*>(bbase);
     const uint32_t bstride = (uint32_t)(G * N * ESZ);
     const int bvalid = (int)(N * ESZ / 16);
+    // head 0's tiles start moving before phase A: after C's loads and the
+    // single copy of B where that copy can be taken, else first (where C's
+    // rows would otherwise stay live across the copy issue: more spilled
+    // registers at N = 256)
+    auto issue_head0 = [&]() {
+        if (nh > 0) {
+            load_vec(0);
+            if (NBX == 2 || !bstage) issue_x(0, smem);
+            if (hc) issue_h(0, hb0);
+        }
+    };
+    if constexpr (!BONE_OK) issue_head0();
     if (bone) {
         // key tiles [0, tps) into the free x buffer, the rest into the C B^T
         // region; rows past the chunk's last token re-read that token (their
@@ -259,23 +274,22 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
     auto off = [&](int row, int ks) {
         return (uint32_t)min(row, qc - 1) * bcs + (uint32_t)min(ks * 16 + hf * 8, nlast);
     };
-    // this wave's C rows, zeroed past the chunk's end and past N where they
-    // are first used (a select here would wait for the loads at once)
-    if (active) {
-        const int jl = rt * 32 + l32;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) creg[ks] = ldg8(cbase + off(jl, ks));
-    }
+    // this wave's C rows, zeroed past the chunk's end and past N: where the
+    // single copy of B can be taken, where they are first used (a select here
+    // would wait for the loads at once, before head 0's copies are issued),
+    // else as they load
     auto mask_creg = [&]() {
         const int jl = rt * 32 + l32;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) creg[ks] = (jl < qc && ks * 16 + hf * 8 < (int)N) ? creg[ks] : zero8<T>();
     };
-    if (nh > 0) {   // head 0's tiles start moving before phase A
-        load_vec(0);
-        if (NBX == 2 || !bstage) issue_x(0, smem);
-        if (hc) issue_h(0, hb0);
+    if (active) {
+        const int jl = rt * 32 + l32;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) creg[ks] = ldg8(cbase + off(jl, ks));
+        if constexpr (!BONE_OK) mask_creg();
     }
+    if constexpr (BONE_OK) issue_head0();
     // round tile kt of C B^T to the operand type and keep it
     auto round_tile = [&](const f32x16& acc, V8& lo, V8& hi) {
 #pragma unroll
@@ -349,7 +363,9 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
         };
         tiles(stg, cbl0);
     } else if (bstage) {
-        if (active) mask_creg();
+        if constexpr (BONE_OK) {
+            if (active) mask_creg();
+        }
         for (int s0 = 0; s0 < RT; s0 += tps) {
             const int s1 = min(s0 + tps, RT);
             if (s0 > 0) lds_barrier();   // the previous slice has been read
@@ -379,7 +395,7 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
             issue_x(0, smem);
         }
     } else if (active) {
-        mask_creg();
+        if constexpr (BONE_OK) mask_creg();
         V8 bnext[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) bnext[ks] = ldg8(bbase + off(l32, ks));
