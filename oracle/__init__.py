@@ -163,11 +163,13 @@ def chunked(x, dt, A, B, C, D, Q: int, init=None):
       cs     [b,H,nc,Q]  in-chunk inclusive prefix sums of dt*A (log of the
                          cumulative products); entries past a ragged chunk's
                          end are NaN
-      S      [b,nc,H,N,P] right-factor chunk states B^T (decayed X)
+      S      [b,nc,H,N,P] chunk states: B^T applied to the chunk's dt-scaled
+                         inputs after their decay (step 2 of the decomposition)
       h_in   [b,nc,H,N,P] state entering each chunk (h_c; h_0 = init, zero if None)
-    Reading of "decayed X": token j of a chunk is weighted by the decay from j
-    to the chunk's end, a_{j+1} ... a_{Q-1}; of "decayed h_c": row j is scaled
-    by a_0 ... a_j. A last chunk shorter than Q is allowed.
+    Reading of the decay in step 2: token j of a chunk is weighted by the decay
+    from j to the chunk's end, a_{j+1} ... a_{Q-1}; of the decay of the entering
+    state in step 4: row j is scaled by a_0 ... a_j. A last chunk shorter than
+    Q is allowed.
     """
     x, dt, A, B, C, D = (np.asarray(v, dtype=np.float64) for v in (x, dt, A, B, C, D))
     b, T, H, P = x.shape
