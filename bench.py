@@ -678,7 +678,19 @@ def main() -> int:
         varlen()
     torch.cuda.synchronize()
     varlen_ms = (time.perf_counter() - tv) * 1e3 / args.steps
-    del yv, seq
+    # and with the output gate (ssd_forward_varlen_gated)
+    zv = inputs.generate_gate(w, seed=1).to(dev)
+    varlen_gated = P(ssd.ssd_forward_varlen_gated, d, g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], None, seq,
+                     zv, yv, final, ws, ws.numel(), sh)
+    for _ in range(args.warmup):
+        varlen_gated()
+    torch.cuda.synchronize()
+    tv = time.perf_counter()
+    for _ in range(args.steps):
+        varlen_gated()
+    torch.cuda.synchronize()
+    varlen_gated_ms = (time.perf_counter() - tv) * 1e3 / args.steps
+    del yv, seq, zv
 
     # context parallelism as one of 8 GPUs would run it (Knowl 8): its share
     # is T/8 tokens of every row; it runs them from a zero state, forms its
@@ -830,7 +842,8 @@ def main() -> int:
                                     "hbm_frac": round(norm_bytes / (norm_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                                     "how": "in place on the gated output, event-timed on the launch stream"}},
         "varlen": {"entry": "ssd_forward_varlen", "documents_per_row": 8, "ms_per_step": round(varlen_ms, 5),
-                   "tokens_per_s": round(w.batch * w.seqlen / (varlen_ms * 1e-3), 1)},
+                   "tokens_per_s": round(w.batch * w.seqlen / (varlen_ms * 1e-3), 1),
+                   "with_gate_ms_per_step": round(varlen_gated_ms, 5)},
         "context_parallel": cp,
         "decode": decode,
         "cpu_baseline": None,

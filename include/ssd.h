@@ -18,7 +18,8 @@
  * (ssd_forward_init, ssd_state_passing_init, ssd_chunk_scan_init); with the
  * block's output gate (ssd_forward_gated) and the norm after it
  * (ssd_gated_rmsnorm); over rows packing several documents
- * (ssd_forward_varlen); one decoding token (ssd_step); the shard chain of
+ * (ssd_forward_varlen, and with the gate ssd_forward_varlen_gated); one
+ * decoding token (ssd_step); the shard chain of
  * sequence parallelism (ssd_total_decay, ssd_fold_states); and sizing,
  * checking and status helpers.
  *
@@ -218,6 +219,21 @@ ssd_status ssd_forward_varlen(const ssd_dims* d, const void* x, const float* dt,
                               const void* B, const void* C, const float* D, const float* initial_state,
                               const int32_t* seq_idx, void* y, float* final_state, void* workspace,
                               size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Packed documents with the output gate: the block of "Transformers are
+ * SSMs", Knowl 6 (y gated by SiLU(z) before the norm) over rows that pack
+ * several documents as in Knowl 8. The same as ssd_forward_varlen, then
+ *   y = y * silu(z),  silu(z) = z / (1 + e^{-z})
+ * elementwise in the chunk scan's epilogue, z [b,T,H,P] in d->dtype (device,
+ * caller-owned, 16-byte aligned, read only, required when b > 0 and T > 0).
+ * final_state is the ungated state. Errors as ssd_forward_varlen, plus
+ * SSD_ERR_NULL_POINTER for a missing z.
+ */
+ssd_status ssd_forward_varlen_gated(const ssd_dims* d, const void* x, const float* dt, const float* A,
+                                    const void* B, const void* C, const float* D, const float* initial_state,
+                                    const int32_t* seq_idx, const void* z, void* y, float* final_state,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Sequence (context) parallelism ("Transformers are SSMs", Knowl 8): a long

@@ -70,6 +70,8 @@ def load_library() -> ctypes.CDLL:
     lib.ssd_forward_gated.restype = st
     lib.ssd_forward_varlen.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.ssd_forward_varlen.restype = st
+    lib.ssd_forward_varlen_gated.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.ssd_forward_varlen_gated.restype = st
     lib.ssd_total_decay.argtypes, lib.ssd_total_decay.restype = [P, vp, vp, vp, vp], st
     lib.ssd_gated_rmsnorm.argtypes = [P, vp, vp, vp, ctypes.c_float, ctypes.c_int64, vp, vp]
     lib.ssd_gated_rmsnorm.restype = st
@@ -342,6 +344,17 @@ def ssd_forward_varlen(d, x, dt, A, B, C, D, initial_state, seq_idx, y, final_st
                                              _ptr(final_state), _ptr(workspace), workspace_bytes, s))
 
 
+def ssd_forward_varlen_gated(d, x, dt, A, B, C, D, initial_state, seq_idx, z, y, final_state, workspace,
+                             workspace_bytes, stream=None):
+    _check_io(d, x=x, dt=dt, A=A, B=B, C=C, D=D, initial_state=initial_state, seq_idx=seq_idx, z=z, y=y,
+              final_state=final_state)
+    _check_workspace(workspace, workspace_bytes, _device_of(final_state))
+    s = _stream(final_state.device) if stream is None else stream
+    _check(_launch("ssd_forward_varlen_gated", ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(B),
+                                                   _ptr(C), _ptr(D), _ptr(initial_state), _ptr(seq_idx), _ptr(z),
+                                                   _ptr(y), _ptr(final_state), _ptr(workspace), workspace_bytes, s))
+
+
 def ssd_gated_rmsnorm(d, y, z, weight, eps, groups, out, stream=None):
     xt, shx = _torch_dtype(d.dtype), _shapes(d)["x"]
     _expect_all([("y", y, shx, xt), ("z", z, shx, xt), ("out", out, shx, xt),
@@ -462,7 +475,8 @@ def forward(x, dt, A, B, C, D, chunk_size: int, state_dtype: str | None = None, 
     ssd_forward_init when initial_state [b,H,N,P] fp32 is given, or
     ssd_forward_gated, y * silu(z), when the gate input z (x's shape and
     type) is given, or ssd_forward_varlen when seq_idx [b,T] int32, the
-    non-decreasing document id of each token, is given; not with z).
+    non-decreasing document id of each token, is given, or
+    ssd_forward_varlen_gated when both are).
 
     state_dtype is the storage of the inter-chunk states in the workspace
     ("fp32" or "bf16"; default: that of x). The running state and the returned
@@ -480,12 +494,17 @@ def forward(x, dt, A, B, C, D, chunk_size: int, state_dtype: str | None = None, 
                                       or tuple(initial_state.shape) != tuple(final.shape)):
         raise ValueError(f"initial_state must be float32 {tuple(final.shape)}")
     if seq_idx is not None:
-        if z is not None:
-            raise ValueError("seq_idx and z together are not supported")
         if seq_idx.dtype != torch.int32 or tuple(seq_idx.shape) != (d.batch, d.seqlen):
             raise ValueError(f"seq_idx must be int32 {(d.batch, d.seqlen)}")
         seq_idx = seq_idx.contiguous()
-        ssd_forward_varlen(d, x, dt, A, B, C, D, initial_state, seq_idx, y, final, workspace, workspace.numel())
+        if z is not None:
+            if z.dtype != x.dtype or z.shape != x.shape:
+                raise ValueError("z must have x's shape and type")
+            ssd_forward_varlen_gated(d, x, dt, A, B, C, D, initial_state, seq_idx, z, y, final, workspace,
+                                     workspace.numel())
+        else:
+            ssd_forward_varlen(d, x, dt, A, B, C, D, initial_state, seq_idx, y, final, workspace,
+                               workspace.numel())
     elif z is not None:
         if z.dtype != x.dtype or z.shape != x.shape:
             raise ValueError("z must have x's shape and type")

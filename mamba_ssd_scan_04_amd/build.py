@@ -34,7 +34,7 @@ FLAGS = [
 # per (input type, state type, variant) from chunk_scan_inst.hip, so that its
 # many template instantiations build in parallel.
 _SC_UNITS = [("chunk_scan_inst.hip", f"chunk_scan_{x}_{s}_{v}", [f"-DSSD_SC_X={x}", f"-DSSD_SC_S={s}", f"-DSSD_SC_V={v}"])
-             for x, s in (("bf16", "bf16"), ("bf16", "f32"), ("f32", "f32")) for v in (0, 1, 2)]
+             for x, s in (("bf16", "bf16"), ("bf16", "f32"), ("f32", "f32")) for v in (0, 1, 2, 3)]
 SOURCES = [(f, os.path.splitext(f)[0], []) for f in
            ("ssd_api.hip", "chunk_cumsum.hip", "chunk_state.hip", "state_passing.hip", "chunk_scan.hip",
             "ssd_step.hip", "shard.hip", "norm.hip")] + _SC_UNITS

@@ -7,7 +7,7 @@
 namespace ssd {
 
 #define SSD_SC_DECL(X, S, V) hipError_t launch_chunk_scan_##X##_##S##_##V(const Params& p, hipStream_t s);
-#define SSD_SC_DECL3(X, S) SSD_SC_DECL(X, S, 0) SSD_SC_DECL(X, S, 1) SSD_SC_DECL(X, S, 2)
+#define SSD_SC_DECL3(X, S) SSD_SC_DECL(X, S, 0) SSD_SC_DECL(X, S, 1) SSD_SC_DECL(X, S, 2) SSD_SC_DECL(X, S, 3)
 SSD_SC_DECL3(bf16, bf16)
 SSD_SC_DECL3(bf16, f32)
 SSD_SC_DECL3(f32, f32)
@@ -15,11 +15,12 @@ SSD_SC_DECL3(f32, f32)
 #undef SSD_SC_DECL
 
 hipError_t launch_chunk_scan(const Params& p, int dtype, int state_dtype, hipStream_t s) {
-    if (p.z && p.seq_idx) return hipErrorInvalidValue;   // no gated instantiation with documents
-    const int v = p.z ? 1 : (p.seq_idx ? 2 : 0);
+    // 0 plain, 1 gated, 2 packed documents, 3 both
+    const int v = (p.z ? 1 : 0) + (p.seq_idx ? 2 : 0);
 #define SSD_SC_PICK(X, S)                                         \
     return v == 1 ? launch_chunk_scan_##X##_##S##_1(p, s)         \
          : v == 2 ? launch_chunk_scan_##X##_##S##_2(p, s)         \
+         : v == 3 ? launch_chunk_scan_##X##_##S##_3(p, s)         \
                   : launch_chunk_scan_##X##_##S##_0(p, s);
     if (dtype == 1 && state_dtype == 1) { SSD_SC_PICK(bf16, bf16) }
     if (dtype == 1) { SSD_SC_PICK(bf16, f32) }

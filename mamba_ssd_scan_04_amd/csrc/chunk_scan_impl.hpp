@@ -47,8 +47,9 @@ constexpr int kScanThreads = 512;
 constexpr int kScanWaves = kScanThreads / 64;
 
 // Instantiations of the chunk scan: the plain kernel, the one with the output
-// gate in its epilogue, and the one with document masks (packed documents).
-enum ScanVariant { kScanPlain = 0, kScanGate = 1, kScanVarlen = 2 };
+// gate in its epilogue, the one with document masks (packed documents), and
+// the one with both.
+enum ScanVariant { kScanPlain = 0, kScanGate = 1, kScanVarlen = 2, kScanGateVarlen = 3 };
 
 template <typename T, int PT, int NT, typename ST>
 struct ScanCfg {
@@ -786,7 +787,8 @@ static hipError_t allow_lds_once(K kern) {
 
 template <typename T, int PT, int NT, typename ST, int NBX, int NBH, bool CBL, int VAR>
 static hipError_t launch_sc2(const Params& p, int hpw, int lds, hipStream_t s) {
-    auto kern = ssd_chunk_scan_kernel<T, PT, NT, ST, NBX, NBH, CBL, VAR == kScanGate, VAR == kScanVarlen>;
+    auto kern = ssd_chunk_scan_kernel<T, PT, NT, ST, NBX, NBH, CBL, VAR == kScanGate || VAR == kScanGateVarlen,
+                                      VAR == kScanVarlen || VAR == kScanGateVarlen>;
     hipError_t e = allow_lds_once(kern);
     if (e != hipSuccess) return e;
     const int64_t nhb = (p.heads_per_group + hpw - 1) / hpw;
@@ -825,7 +827,7 @@ static hipError_t launch_sc(const Params& p, hipStream_t s) {
     const int hpw = scan_hpw(p);
     // prefer C B^T in LDS (frees the registers that would hold it), then
     // double-buffered copies
-    const bool vl = VAR == kScanVarlen;
+    const bool vl = VAR == kScanVarlen || VAR == kScanGateVarlen;
 #define SSD_SC_TRY(NBX_, NBH_, CBL_)                                                           \
     if (Cfg::lds(Q, NBX_, NBH_, CBL_, vl) <= kScanMaxLds)                                      \
         return launch_sc2<T, PT, NT, ST, NBX_, NBH_, CBL_, VAR>(p, hpw, Cfg::lds(Q, NBX_, NBH_, CBL_, vl), s);

@@ -1,6 +1,7 @@
 // One (input type, state type, variant) of the chunk-scan kernel; the build
 // compiles this file once per combination with SSD_SC_X (bf16 | f32),
-// SSD_SC_S (bf16 | f32) and SSD_SC_V (0 plain, 1 gated, 2 packed documents).
+// SSD_SC_S (bf16 | f32) and SSD_SC_V (0 plain, 1 gated, 2 packed documents, 3 gated
+// packed documents).
 #include "chunk_scan_impl.hpp"
 
 #if !defined(SSD_SC_X) || !defined(SSD_SC_S) || !defined(SSD_SC_V)

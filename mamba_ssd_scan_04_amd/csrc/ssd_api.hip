@@ -294,6 +294,26 @@ ssd_status forward_impl(const ssd_dims* d, const void* x, const float* dt, const
     return st;
 }
 
+
+// packed documents, with the output gate when z is given
+ssd_status varlen_impl(const ssd_dims* d, const void* x, const float* dt, const float* A, const void* B,
+                       const void* C, const float* D, const float* initial_state, const int32_t* seq_idx,
+                       const void* z, void* y, float* final_state, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+    ssd_status st = ssd_check_dims(d);
+    if (st != SSD_OK) return st;
+    if (empty(d)) return forward_impl(d, x, dt, A, B, C, D, initial_state, nullptr, y, final_state, workspace,
+                                      workspace_bytes, stream);
+    if (!seq_idx) return SSD_ERR_NULL_POINTER;
+    if (reinterpret_cast<uintptr_t>(seq_idx) & 3) return SSD_ERR_MISALIGNED;
+    // the chunk scan keeps the chunk's document ids in LDS beside its tiles
+    if (ssd::chunk_scan_lds_bytes(d->dtype, d->state_dtype, d->headdim, d->dstate, d->chunk_size) +
+            4 * (d->chunk_size < 32 ? 32 : d->chunk_size) > kMaxLds)
+        return SSD_ERR_UNSUPPORTED;
+    return forward_impl(d, x, dt, A, B, C, D, initial_state, z, y, final_state, workspace, workspace_bytes,
+                        stream, seq_idx);
+}
+
 }  // namespace
 
 extern "C" {
@@ -431,18 +451,17 @@ ssd_status ssd_forward_varlen(const ssd_dims* d, const void* x, const float* dt,
                               const void* B, const void* C, const float* D, const float* initial_state,
                               const int32_t* seq_idx, void* y, float* final_state, void* workspace,
                               size_t workspace_bytes, hipStream_t stream) {
-    ssd_status st = ssd_check_dims(d);
-    if (st != SSD_OK) return st;
-    if (empty(d)) return forward_impl(d, x, dt, A, B, C, D, initial_state, nullptr, y, final_state, workspace,
-                                      workspace_bytes, stream);
-    if (!seq_idx) return SSD_ERR_NULL_POINTER;
-    if (reinterpret_cast<uintptr_t>(seq_idx) & 3) return SSD_ERR_MISALIGNED;
-    // the chunk scan keeps the chunk's document ids in LDS beside its tiles
-    if (ssd::chunk_scan_lds_bytes(d->dtype, d->state_dtype, d->headdim, d->dstate, d->chunk_size) +
-            4 * (d->chunk_size < 32 ? 32 : d->chunk_size) > kMaxLds)
-        return SSD_ERR_UNSUPPORTED;
-    return forward_impl(d, x, dt, A, B, C, D, initial_state, nullptr, y, final_state, workspace, workspace_bytes,
-                        stream, seq_idx);
+    return varlen_impl(d, x, dt, A, B, C, D, initial_state, seq_idx, nullptr, y, final_state, workspace,
+                       workspace_bytes, stream);
+}
+
+ssd_status ssd_forward_varlen_gated(const ssd_dims* d, const void* x, const float* dt, const float* A,
+                                    const void* B, const void* C, const float* D, const float* initial_state,
+                                    const int32_t* seq_idx, const void* z, void* y, float* final_state,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (d && d->batch > 0 && d->seqlen > 0 && !z) return SSD_ERR_NULL_POINTER;
+    return varlen_impl(d, x, dt, A, B, C, D, initial_state, seq_idx, z, y, final_state, workspace,
+                       workspace_bytes, stream);
 }
 
 // shapes of a per-head state: b >= 0, H, N, P in the supported lists

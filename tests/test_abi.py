@@ -266,6 +266,22 @@ def test_varlen_forward_argument_errors(lib):
     assert f(P(dims(batch=0)), None, None, None, None, None, None, None, None, None, None, None, 0, None) == OK
 
 
+def test_varlen_gated_forward_argument_errors(lib):
+    d = dims()
+    ws = ssd.ssd_workspace_size(d)
+    good = [_fake(0x700000 * (i + 1)) for i in range(11)]
+    x, dt, A, B, C, D, seq, z, y, fin, work = good
+    f = lib.ssd_forward_varlen_gated
+    P = ctypes.byref
+    assert f(P(d), x, dt, A, B, C, D, None, seq, None, y, fin, work, ws, None) == NULLP     # z required
+    assert f(P(d), x, dt, A, B, C, D, None, None, z, y, fin, work, ws, None) == NULLP     # seq_idx required
+    assert f(P(d), x, dt, A, B, C, D, None, _fake(0x700002), z, y, fin, work, ws, None) == MISAL
+    assert f(P(d), x, dt, A, B, C, D, None, seq, _fake(0x700008), y, fin, work, ws, None) == MISAL
+    assert f(P(d), x, dt, A, B, C, D, None, seq, z, y, fin, work, ws - 1, None) == WS
+    assert f(P(dims(ngroups=3)), x, dt, A, B, C, D, None, seq, z, y, fin, work, ws, None) == SHAPE
+    assert f(P(dims(batch=0)), *([None] * 12), 0, None) == OK
+
+
 def test_shard_entry_points_argument_errors(lib):
     P = ctypes.byref
     a = _fake(0x600000)
