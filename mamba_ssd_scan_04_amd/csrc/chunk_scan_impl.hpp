@@ -87,9 +87,10 @@ __device__ __forceinline__ typename Vec8<T>::type x_frag(const unsigned char* xt
 // GATE: y *= silu(z) in the epilogue (a separate instantiation, so that the
 // plain kernel carries none of its registers). VARLEN: packed documents
 // ("Transformers are SSMs", Knowl 8: the decay is 0 at a document start): the
-// masked product keeps only key tokens of the query's document, and the
-// carried state reaches only rows in the document of the token before the
-// chunk (its own instantiation too).
+// masked product keeps only key tokens of the query's document (folded once
+// into the chunk's C B^T, which does not depend on the head), and the carried
+// state reaches only rows in the document of the token before the chunk (its
+// own instantiation too).
 template <typename T, int PT, int NT, typename ST, int NBX, int NBH, bool CBL, bool GATE, bool VARLEN>
 __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, int hpw) {
     using Cfg = ScanCfg<T, PT, NT, ST>;
@@ -436,8 +437,54 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
     }
     wait_vmem();
     lds_barrier();
-    int sqj = 0;   // this lane's query token's document (VARLEN)
-    if constexpr (VARLEN) sqj = active ? sqv[rt * 32 + l32] : 0;
+    // packed documents: this lane's query token's document, and the first
+    // token of that document within the chunk (0 when it started before the
+    // chunk), found by a binary search over the chunk's ids. Ids do not
+    // decrease along T, so a key i of the chunk lies in the query's document
+    // iff i >= that first token (a key after the query is masked as
+    // non-causal anyway).
+    int sqj = 0, dstart = 0;
+    if constexpr (VARLEN) {
+        if (active) {
+            const int jq = rt * 32 + l32;
+            sqj = sqv[jq];
+#pragma unroll
+            for (int step = 128; step >= 1; step >>= 1)
+                if (dstart + step <= jq && sqv[dstart + step - 1] < sqj) dstart += step;
+            // The document mask depends on the (query, key) pair only, not on
+            // the head: it is folded once into this wavefront's row of C B^T
+            // tiles, which every head then uses as they are. Element idx of
+            // tile kt holds key kt*32 + 4hf + 8(idx/4) + idx%4; keys before
+            // dstart lie in an earlier document and their C B^T value is set
+            // to 0 (exact: their decay factor is at most 1). Tiles no lane of
+            // the wavefront needs to mask are left alone.
+            auto mask8 = [&](V8& v, int ds, int e0) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int idx = e0 + e, off = 8 * (idx >> 2) + (idx & 3);
+                    v[e] = off >= ds ? v[e] : from_f32<T>(0.0f);
+                }
+            };
+            for (int kt = 0; kt <= rt; ++kt) {
+                const int ds = dstart - (kt * 32 + 4 * hf);
+                if (__builtin_amdgcn_readfirstlane(__any(ds > 0) ? 1 : 0) == 0) continue;
+                if (kt == rt) {
+                    mask8(cbd[0], ds, 0);
+                    mask8(cbd[1], ds, 8);
+                } else if constexpr (CBL) {
+                    T* tp = reinterpret_cast<T*>(cbw + kt * Cfg::CBTILE);
+                    V8 lo = load8(tp + lane * 8), hi = load8(tp + (64 + lane) * 8);
+                    mask8(lo, ds, 0);
+                    mask8(hi, ds, 8);
+                    store8(tp + lane * 8, lo);
+                    store8(tp + (64 + lane) * 8, hi);
+                } else {
+                    mask8(cb[kt < 7 ? kt : 6][0], ds, 0);
+                    mask8(cb[kt < 7 ? kt : 6][1], ds, 8);
+                }
+            }
+        }
+    }
 
     // ---- phase B: heads ----
     // One head: load the next head's vectors, compute this head from xt / ht /
@@ -461,7 +508,6 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
     struct Stage {
         V8 m[2];
         float u, d, r;
-        int s;   // key token's document (VARLEN)
         V8 xf[2][PT];
     };
     const int bcl = 8 * ((lane & 15) >> 2) + 4 * (lane >> 5) + (lane & 3);   // key token of this lane's slot
@@ -551,7 +597,6 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
                 st.r = c2v[k * 32 + 31];
                 st.u = (off ? uv : c2v)[k * 32 + bcl];
                 st.d = dtv[k * 32 + bcl];
-                if constexpr (VARLEN) st.s = sqv[k * 32 + bcl];
 #pragma unroll
                 for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
@@ -568,8 +613,6 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
                     static_for<16>([&](auto I) {
                         constexpr int idx = decltype(I)::value;
                         float val = row_bcast<idx>(st.u) * (to_f32(st.m[idx >> 3][idx & 7]) * vj);
-                        if constexpr (VARLEN)
-                            val = __float_as_int(row_bcast<idx>(__int_as_float(st.s))) == sqj ? val : 0.0f;
                         aop[idx >> 3][idx & 7] = from_f32<T>(val);
                     });
                 } else {
@@ -577,9 +620,7 @@ __global__ __launch_bounds__(kScanThreads) void ssd_chunk_scan_kernel(Params p, 
                     static_for<16>([&](auto I) {
                         constexpr int idx = decltype(I)::value;
                         constexpr int off = 8 * (idx >> 2) + (idx & 3);
-                        float pen = __int_as_float(((dj - off) >> 31) & (int)0xff800000u);
-                        if constexpr (VARLEN)
-                            pen = __float_as_int(row_bcast<idx>(__int_as_float(st.s))) == sqj ? pen : -INFINITY;
+                        const float pen = __int_as_float(((dj - off) >> 31) & (int)0xff800000u);
                         aop[idx >> 3][idx & 7] = from_f32<T>(
                             to_f32(cbd[idx >> 3][idx & 7]) * fast_exp2((c2j - row_bcast<idx>(st.u)) + pen) *
                             row_bcast<idx>(st.d));
