@@ -17,7 +17,8 @@
 // Work split. One workgroup (4 wavefronts) takes one chunk and up to HPW heads
 // of one group, which share B (fewer heads, more workgroups, when the grid
 // would not fill the chip). The chunk is consumed in blocks of 32 tokens
-// through a ring of NBUF LDS buffers: while the matrix cores work on block k,
+// through a ring of NBUF LDS buffers (three when x streams from HBM, two when
+// it stays in the last-level cache): while the matrix cores work on block k,
 // buffer loads straight to LDS (no registers) fill blocks k+1 .. k+NBUF-1, and
 // the barrier between blocks does not drain them (lds_barrier). B and x blocks
 // stay token-major in LDS (swizzled rows); the token-contiguous operand
@@ -55,8 +56,13 @@ struct StateCfg {
     // CU let one's stores and prologue overlap the other's copies and math.
     // side tile: dt [HPW][Q], overwritten in place by w
     static constexpr int SIDE = HPW * 256 * 4;
-    static constexpr int NBUF = 2 * (3 * BUF + SIDE) <= 160 * 1024 ? 3 : 2;
-    static constexpr int LDS = NBUF * BUF + SIDE;
+    static constexpr int NBUF3 = 2 * (3 * BUF + SIDE) <= 160 * 1024 ? 3 : 2;
+    // x streamed from HBM (non-temporal copies) keeps NBUF3 buffers; x that
+    // stays in the last-level cache is copied one block ahead only (two
+    // buffers), since from that cache one block in flight covers the latency
+    // and a second one only delays the block needed next
+    template <bool XNT> static constexpr int nbuf() { return XNT ? NBUF3 : 2; }
+    template <bool XNT> static constexpr int lds() { return nbuf<XNT>() * BUF + SIDE; }
     static constexpr int NDB = (kStateKB * BRC / 64 + 3) / 4;  // B copy instructions per wave
     static constexpr int NDX = (kStateKB * XRC / 64 + 3) / 4;  // x copy instructions per wave per head
 };
@@ -111,8 +117,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     using V8 = typename Vec8<T>::type;
     constexpr int HPW = Cfg::HPW, WPH = Cfg::WPH, PTW = Cfg::PTW;
     constexpr int ESZ = (int)sizeof(T);
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[Cfg::LDS];
-    constexpr int NBUF = Cfg::NBUF;
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[Cfg::template lds<XNT>()];
+    constexpr int NBUF = Cfg::template nbuf<XNT>();
     float* wv = reinterpret_cast<float*>(smem + NBUF * Cfg::BUF);   // [HPW][QT]: dt, then w
 
     // Q: tokens per chunk; QT: its rows as tiled, whole 32-token blocks (a
