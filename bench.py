@@ -88,6 +88,7 @@ def attainable_peaks(torch, stream) -> dict | None:
     lib.ssd_peak_mfma_bf16.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
     lib.ssd_peak_stream.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
                                     ctypes.c_void_p]
+    lib.ssd_peak_stream_pieces.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
     sh = ctypes.c_void_p(stream.cuda_stream)
 
     def timed(fn, reps):
@@ -123,16 +124,28 @@ def attainable_peaks(torch, stream) -> dict | None:
         if rc != 0:
             raise RuntimeError(f"ssd_peak_stream failed ({rc})")
 
+    def stream_pieces():
+        rc = lib.ssd_peak_stream_pieces(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
+                                        nbytes // 16, sh)
+        if rc != 0:
+            raise RuntimeError(f"ssd_peak_stream_pieces failed ({rc})")
+
     t = timed(stream_copy, 10)
-    stream_gbs = 2 * nbytes / t / 1e9
+    grid_gbs = 2 * nbytes / t / 1e9
+    t = timed(stream_pieces, 10)
+    piece_gbs = 2 * nbytes / t / 1e9
+    stream_gbs = max(grid_gbs, piece_gbs)
     t = timed(lambda: dst.copy_(src), 10)
     copy_gbs = 2 * nbytes / t / 1e9
     del src, dst
     return {"mfma_bf16_TFLOP/s": round(mfma_tfs, 1), "mfma_bf16_frac_of_peak": round(mfma_tfs / MFMA_BF16_PEAK_TFS, 4),
             "stream_GB/s": round(stream_gbs, 1), "stream_frac_of_peak": round(stream_gbs / HBM_PEAK_GBS, 4),
+            "stream_4kb_pieces_GB/s": round(piece_gbs, 1), "stream_grid_stride_GB/s": round(grid_gbs, 1),
             "torch_copy_GB/s": round(copy_gbs, 1),
             "how": "MFMA: 2048 workgroups x 4 waves x 8000 chained v_mfma_f32_32x32x16_bf16; "
-                   "stream: 1 GiB read + 1 GiB write, 16-byte non-temporal vectors, 16384 workgroups; torch copy_: the same 1 GiB"}
+                   "stream: the faster of two copies of 1 GiB (read + write) with 16-byte non-temporal vectors, one "
+                   "contiguous 4 KB piece per workgroup (262144 workgroups) or grid-stride over 16384 workgroups "
+                   "with 4 loads in flight per thread; torch copy_: the same 1 GiB"}
 
 
 def streams_x(w, state_esz: int) -> bool:

@@ -225,6 +225,10 @@ def test_peak_probe_library_exports():
     assert peak.ssd_peak_mfma_bf16(4, 10, None, None) != 0
     assert peak.ssd_peak_stream(_fake(0x1000), _fake(0x2000), 0, 4, None) != 0
     assert peak.ssd_peak_stream(_fake(0x1008), _fake(0x2000), 16, 4, None) != 0
+    peak.ssd_peak_stream_pieces.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    assert peak.ssd_peak_stream_pieces(_fake(0x1000), _fake(0x2000), 0, None) != 0
+    assert peak.ssd_peak_stream_pieces(_fake(0x1000), _fake(0x2008), 16, None) != 0
+    assert peak.ssd_peak_stream_pieces(None, _fake(0x2000), 16, None) != 0
     # the chunk scan's traffic probe: a null pointer, then shapes it does not
     # cover (T not a multiple of Q, Q above 256, P not a multiple of 8, a tile
     # that is not whole 64-lane groups), all rejected before any launch

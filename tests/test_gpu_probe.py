@@ -90,3 +90,28 @@ def test_state_traffic_probe_copies(shape, nt):
     last = x.view(b, nc, Q, H, P)[:, :, -32:].permute(0, 1, 3, 2, 4)
     want = last.unsqueeze(3).expand(-1, -1, -1, N // 32, -1, -1)
     assert torch.equal(st.view(want.shape), want)
+
+
+@pytest.mark.parametrize("nvec", [1, 255, 256, 257, 4096 * 3 + 5])
+def test_stream_probes_copy_exactly(nvec):
+    """Both streaming copies of the attainable-peak figure (grid-stride, and
+    one 4 KB piece per workgroup) copy exactly n 16-byte vectors: every
+    vector, including a ragged last piece, and nothing past the end."""
+    path = os.path.join(os.path.dirname(ssd.LIB_PATH), "libssd_peak.so")
+    if not os.path.exists(path):
+        pytest.skip("libssd_peak.so not built")
+    print(f"stream probes nvec={nvec}", flush=True)
+    lib = ctypes.CDLL(path)
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.ssd_peak_stream.argtypes = [vp, vp, i64, i64, vp]
+    lib.ssd_peak_stream_pieces.argtypes = [vp, vp, i64, vp]
+    dev = torch.device("cuda:0")
+    src = torch.arange(nvec * 4 + 4, dtype=torch.int32, device=dev)
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for call in (lambda d: lib.ssd_peak_stream(src.data_ptr(), d.data_ptr(), nvec, 4, s),
+                 lambda d: lib.ssd_peak_stream_pieces(src.data_ptr(), d.data_ptr(), nvec, s)):
+        dst = torch.full_like(src, -1)
+        assert call(dst) == 0
+        torch.cuda.synchronize()
+        assert torch.equal(dst[:nvec * 4], src[:nvec * 4])
+        assert torch.equal(dst[nvec * 4:], torch.full((4,), -1, dtype=torch.int32, device=dev))
