@@ -86,3 +86,31 @@ def test_streaming_copies_ragged_whole_output():
         record_parity("forward", w.name, sd, errs[sd][0].value(), errs[sd][1].value(), tol)
     for sd in outs:
         assert errs[sd][0].value() <= tol and errs[sd][1].value() <= tol, sd
+
+
+@pytest.mark.parametrize("name", ["m2p7", "long16k"])
+def test_fullsize_gated_whole_output(name):
+    """ssd_forward_gated (the output gate y * silu(z) in the chunk scan's
+    epilogue, "Transformers are SSMs", Knowl 6) at full size with the states
+    stored in bf16, as the benchmark times it, against the oracle's recurrence
+    followed by the fp64 gate, over every output element; the final state is
+    the ungated one."""
+    import oracle
+
+    w = inputs.WORKLOADS[name]
+    say(f"fullsize gated {name} {w.describe()}")
+    inp = inputs.generate(w, seed=0)
+    z = inputs.generate_gate(w, seed=1)
+    dev = to_dev(inp)
+    y, fin = ssd.forward(dev["x"], dev["dt"], dev["A"], dev["B"], dev["C"], dev["D"], w.chunk_size, "bf16",
+                         z=z.to("cuda"))
+    torch.cuda.synchronize()
+    assert torch.isfinite(y.float()).all() and torch.isfinite(fin).all()
+    ey, ef = MaxRelErr(), MaxRelErr()
+    for b in range(w.batch):
+        y_ref, fin_ref = oracle_batch(inp, b)
+        ey.add(y[b].float().cpu().numpy(), oracle.silu_gate(y_ref[0], z[b].float().numpy()))
+        ef.add(fin[b].cpu().numpy(), fin_ref[0])
+    tol = TOL[w.dtype]
+    record_parity("gated", name, "bf16", ey.value(), ef.value(), tol)
+    assert ey.value() <= tol and ef.value() <= tol
