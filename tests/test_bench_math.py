@@ -51,3 +51,16 @@ def test_flops_match_the_definitions():
     assert work["ssd_chunk_state"]["flops"] == 2 * b * T * H * N * P + b * T * H
     tri = Q * (Q + 1)
     assert work["ssd_chunk_scan"]["flops"] == b * nc * (G * N * tri + H * P * tri) + 2 * b * (T - Q) * H * N * P
+
+
+def test_traffic_records_match_the_kernel_sources():
+    """The committed rocprofv3 traffic records (profiles/pmc_*.json) were taken
+    on the current kernel sources, so the benchmark reports the dominant
+    kernel's measured HBM bytes (roofline.traffic) instead of null; and each
+    record's bytes stay within 2% of the kernel's algorithmic bytes."""
+    for kern in bench.KERNELS:
+        for sd in ("bf16", "fp32"):
+            got = bench.measured_traffic(kern, "m2p7", sd)
+            assert got is not None, f"{kern} {sd}: no record for the current source"
+            alg = bench.kernel_work(inputs.WORKLOADS["m2p7"], 2 if sd == "bf16" else 4)[kern]["bytes"]
+            assert abs(got / alg - 1.0) < 0.02, (kern, sd, got, alg)
